@@ -1,0 +1,102 @@
+"""Weight and activation quantisers of the fused MoE layer (CPU oracle).
+
+TEST INFRASTRUCTURE ONLY: nothing on the GPU path may import this module.
+
+* MXFP4 weights (flashinfer PR #3738, "perf: optimize MXFP4xBF16 & INT4xFP8 and
+  add MXFP4xFP8 CUTLASS MoE backend for SM90", Description): E2M1 elements with
+  one E8M0 scale per 32 consecutive elements along K.  The shared exponent
+  follows the OCP Microscaling v1.0 conversion: X = floor(log2(max|v|)) - emax,
+  emax = 2 for E2M1, then each element is v / 2^X rounded to nearest-even on
+  the E2M1 grid and clamped to +-6.  A block whose magnitudes are all zero gets
+  scale code 127 (1.0).  X below -127 is clamped to -127 (the smallest E8M0).
+* INT4 weights (same page, Description: "INT4 weight + FP8 activation"; group
+  size named in the review of prepare()): symmetric two's complement codes with
+  one float32 scale per 128 consecutive K elements, s = amax/7 (float32
+  division), q = round-half-even(w/s) clamped to [-8, 7]; an all-zero group
+  gets s = 1.
+* Per-token E4M3 activations (same page, Implementation Notes: per-token
+  activation scales computed while expanding routed rows): s = amax/448 in
+  float32, q = E4M3(x/s) with float32 division; an all-zero token gets s = 1.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import formats as F
+
+MX_BLOCK = 32
+INT4_GROUP = 128
+
+
+def floor_log2(a: np.ndarray) -> np.ndarray:
+    """floor(log2(a)) for positive finite a, exactly (via frexp: a = m*2^e with
+    m in [0.5, 1), so floor(log2 a) = e - 1)."""
+    _, e = np.frexp(np.asarray(a, dtype=np.float64))
+    return e.astype(np.int64) - 1
+
+
+def mxfp4_quantize(w: np.ndarray):
+    """w: float32 [N, K] (K % 32 == 0) -> (codes uint8 [N, K/2], scales uint8 [N, K/32])."""
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    assert k % MX_BLOCK == 0
+    blk = w.reshape(n, k // MX_BLOCK, MX_BLOCK).astype(np.float64)
+    amax = np.max(np.abs(blk), axis=-1)
+    nz = amax > 0
+    x = np.where(nz, floor_log2(np.where(nz, amax, 1.0)) - F.E2M1_EMAX, 0)
+    x = np.maximum(x, -127)
+    scale_code = (x + 127).astype(np.uint8)
+    v = np.ldexp(blk, -x[..., None])  # exact power-of-two scaling in float64
+    codes = F.e2m1_encode(v).reshape(n, k)
+    return F.pack_nibbles(codes), scale_code
+
+
+def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Packed MXFP4 [N, K/2] + E8M0 [N, K/32] -> float64 [N, K] (exact)."""
+    n = codes.shape[0]
+    el = F.e2m1_decode(F.unpack_nibbles(codes))
+    k = el.shape[1]
+    sc = F.e8m0_decode(scales)
+    return (el.reshape(n, k // MX_BLOCK, MX_BLOCK) * sc[..., None]).reshape(n, k)
+
+
+def int4_quantize(w: np.ndarray):
+    """w: float32 [N, K] (K % 128 == 0) -> (codes uint8 [N, K/2], scales float32 [N, K/128])."""
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    assert k % INT4_GROUP == 0
+    grp = w.reshape(n, k // INT4_GROUP, INT4_GROUP)
+    amax = np.max(np.abs(grp), axis=-1)
+    s = np.where(amax > 0, amax / np.float32(7.0), np.float32(1.0)).astype(np.float32)
+    r = (grp / s[..., None]).astype(np.float32)
+    q = np.clip(np.rint(r), -8, 7).astype(np.int64).reshape(n, k)
+    return F.pack_nibbles((q & 0xF).astype(np.uint8)), s
+
+
+def int4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    n = codes.shape[0]
+    q = F.int4_decode(F.unpack_nibbles(codes)).astype(np.float64)
+    k = q.shape[1]
+    return (q.reshape(n, k // INT4_GROUP, INT4_GROUP)
+            * scales.astype(np.float64)[..., None]).reshape(n, k)
+
+
+def e4m3_rows(x: np.ndarray):
+    """Row-wise E4M3 quantisation: x float32 [R, C] -> (codes uint8 [R, C], s float32 [R])."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    s = np.where(amax > 0, amax / np.float32(F.E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    v = (x / s[:, None]).astype(np.float32)
+    return F.e4m3_encode(v), s
+
+
+def mx_exponent_spread(scales: np.ndarray) -> int:
+    """Largest per-row spread of E8M0 codes (max - min).  The float64 GEMM of
+    E4M3 x MXFP4 operands is exact, whatever the summation order, when this
+    spread stays small (each product is a multiple of 2^(Xmin-10) and the sum
+    stays below 2^(24.4+Xmax) for K <= 8192, so it needs at most 34.4 + spread
+    significant bits)."""
+    s = np.asarray(scales, dtype=np.int64)
+    if s.size == 0:
+        return 0
+    return int(np.max(s.max(axis=-1) - s.min(axis=-1)))

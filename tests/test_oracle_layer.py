@@ -1,0 +1,261 @@
+"""Pins of the oracle's layer: brute-force router, exact rational GEMMs, a
+hand-derived single-expert example, reductions (E=1/k=1, identical experts),
+per-token independence and empty inputs (CPU only)."""
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import moe_inputs as MI
+import oracle as O
+from oracle import formats as F
+from oracle import quant as Q
+
+
+def frac_to_f32(fr: Fraction) -> float:
+    """Exact rational -> nearest float32 (ties to even), by integer arithmetic."""
+    if fr == 0:
+        return 0.0
+    sign = -1.0 if fr < 0 else 1.0
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)                      # subnormals share the 2^-149 quantum
+    m = a / Fraction(2) ** (e - 23)       # in [2^23, 2^24) for normals
+    fl = math.floor(m)
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * float(np.float32(math.ldexp(fl, e - 23)))
+
+
+def _make_experts(seed, e_num, hidden, inter, wfmt):
+    out = {}
+    for e, w1, w2 in MI.expert_weights_many(seed, range(e_num), hidden, inter, threads=4):
+        out[e] = O.quantize_expert(w1, w2, wfmt)
+    return out
+
+
+# ----------------------------------------------------------------------------- router
+
+def test_router_brute_force_with_ties():
+    rng = np.random.default_rng(12)
+    for trial in range(300):
+        e = int(rng.integers(2, 9))
+        k = int(rng.integers(1, e + 1))
+        # few distinct values -> many exact ties; include -0.0 and 0.0
+        pool = np.float32([-1.5, -0.0, 0.0, 0.25, 0.25, 1.0, 2.0])
+        logits = rng.choice(pool, size=(3, e)).astype(np.float32)
+        ids, w = O.route(logits, k)
+        for t in range(3):
+            l = logits[t]
+            valid = []
+            for sub in itertools.combinations(range(e), k):
+                s = set(sub)
+                if all((l[i] > l[j]) or (l[i] == l[j] and i < j) for i in s for j in range(e) if j not in s):
+                    valid.append(sub)
+            assert len(valid) == 1
+            order = sorted(valid[0], key=lambda i: (-float(l[i]), i))
+            assert ids[t].tolist() == order, (l, ids[t], order)
+            ref = scipy.special.softmax(l[order].astype(np.float64))
+            assert np.allclose(w[t], ref, rtol=1e-6, atol=1e-7)
+
+
+def test_router_invariants():
+    rng = np.random.default_rng(1)
+    logits = rng.standard_normal((50, 16)).astype(np.float32)
+    ids, w = O.route(logits, 1)
+    assert np.all(w == 1.0)
+    assert np.array_equal(ids[:, 0], np.argmax(logits, axis=1))
+    ids, w = O.route(logits, 16)
+    full = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    assert np.allclose(w, np.take_along_axis(full, ids.astype(np.int64), 1), rtol=1e-6)
+    ids, w = O.route(logits, 5)
+    assert np.all(np.diff(w, axis=1) <= 0)
+    assert np.allclose(w.sum(1), 1.0, atol=1e-6)
+    assert all(len(set(r)) == 5 for r in ids.tolist())
+    # permuting expert columns permutes the ids (no ties in N(0,1) draws)
+    perm = rng.permutation(16)
+    ids_p, w_p = O.route(logits[:, perm], 5)
+    assert np.array_equal(perm[ids_p], ids) and np.array_equal(w_p, w)
+
+
+def test_expand_structure():
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal((40, 10)).astype(np.float32)
+    ids, _ = O.route(logits, 3)
+    off, tok, slot, slot_row = O.expand(ids, 10)
+    assert off[0] == 0 and off[-1] == 120
+    assert np.array_equal(np.diff(off), np.bincount(ids.reshape(-1), minlength=10))
+    for e in range(10):
+        r = np.arange(off[e], off[e + 1])
+        assert np.all(ids[tok[r], slot[r]] == e)
+        assert np.all(np.diff(tok[r]) > 0)
+    assert np.array_equal(slot_row[tok, slot], np.arange(120))
+
+
+# ----------------------------------------------------------------------------- exact GEMMs
+
+@pytest.mark.parametrize("wfmt,afmt", [("mxfp4", "fp8"), ("mxfp4", "bf16"), ("int4", "fp8")])
+def test_gemms_against_exact_rationals(wfmt, afmt):
+    wl = MI.small_workload(tokens=3, experts=4, top_k=2, hidden=128, inter=128,
+                           wfmt=wfmt, afmt=afmt, seed=77)
+    hb = MI.hidden_bf16(wl.seed, wl.tokens, wl.hidden)
+    lg = MI.router_logits(wl.seed, wl.tokens, wl.experts)
+    ex = _make_experts(wl.seed, wl.experts, wl.hidden, wl.inter, wfmt)
+    r = O.forward(hb, lg, wl.top_k, lambda e: ex[e], wfmt, afmt, keep_y1=True)
+    x = F.bf16_to_f32(hb)
+    if afmt == "fp8":
+        a_dec = [[Fraction(float(v)) for v in F.e4m3_decode(row)] for row in r["token_codes"]]
+    else:
+        a_dec = [[Fraction(float(v)) for v in row] for row in x]
+    off = r["offsets"]
+    mism = 0
+    total = 0
+    for e in range(wl.experts):
+        if off[e + 1] == off[e]:
+            continue
+        w1 = O.layer.decode_weight(ex[e].w1q, ex[e].w1s, wfmt)
+        w2 = O.layer.decode_weight(ex[e].w2q, ex[e].w2s, wfmt)
+        w1f = [[Fraction(float(v)) for v in row] for row in w1]
+        w2f = [[Fraction(float(v)) for v in row] for row in w2]
+        for row in range(off[e], off[e + 1]):
+            t = r["row_token"][row]
+            s = Fraction(float(r["token_scales"][t]))
+            for n in range(0, 2 * wl.inter, 7):
+                acc = sum(a * b for a, b in zip(a_dec[t], w1f[n]))
+                exp = frac_to_f32(acc * s)
+                got = float(r["y1"][row, n])
+                total += 1
+                if got != exp:
+                    mism += 1
+                    assert abs(got - exp) <= abs(exp) * 2.0 ** -23, (row, n, got, exp)
+            if afmt == "fp8":
+                a2 = [Fraction(float(v)) for v in F.e4m3_decode(r["fc2_codes"][row])]
+            else:
+                a2 = [Fraction(float(v)) for v in F.bf16_to_f32(r["fc2_codes"][row])]
+            s2 = Fraction(float(r["fc2_scales"][row]))
+            for n in range(0, wl.hidden, 5):
+                acc = sum(a * b for a, b in zip(a2, w2f[n]))
+                exp = frac_to_f32(acc * s2)
+                got = float(r["y2"][row, n])
+                total += 1
+                if got != exp:
+                    mism += 1
+                    assert abs(got - exp) <= abs(exp) * 2.0 ** -23, (row, n, got, exp)
+    assert mism <= max(1, total // 100)
+
+
+def test_fp64_gemm_is_order_independent():
+    wl = MI.small_workload(tokens=8, experts=2, top_k=1, hidden=2048, inter=256, seed=5)
+    hb = MI.hidden_bf16(wl.seed, wl.tokens, wl.hidden)
+    q, s = Q.e4m3_rows(F.bf16_to_f32(hb))
+    w1, _ = MI.expert_weights(wl.seed, 0, wl.hidden, wl.inter)
+    wq, ws = Q.mxfp4_quantize(w1)
+    a = F.e4m3_decode(q)
+    w = Q.mxfp4_decode(wq, ws)
+    r1 = a @ w.T
+    r2 = a[:, ::-1] @ w[:, ::-1].T
+    r3 = sum(a[:, i::7] @ w[:, i::7].T for i in range(7))
+    assert np.array_equal(r1, r2) and np.array_equal(r1, r3)
+
+
+# ----------------------------------------------------------------------------- whole layer
+
+def test_hand_derived_single_expert():
+    """T=1, E=1, k=1, H=32, I=32, MXFP4 x FP8; values chosen so every step is
+    derivable by hand.  gate rows 0.5, up rows 0.25 (up row 0: -0.25),
+    W2 rows 1.0 (even n) / 0.5 (odd n), hidden all 1.0."""
+    h, i = 32, 32
+    hb = F.bf16_rne(np.ones((1, h), dtype=np.float32))
+    w1 = np.concatenate([np.full((i, h), 0.5), np.full((i, h), 0.25)]).astype(np.float32)
+    w1[i] = -0.25
+    w2 = np.where(np.arange(h)[:, None] % 2 == 0, 1.0, 0.5) * np.ones((h, i))
+    ew = O.quantize_expert(w1, w2.astype(np.float32), "mxfp4")
+    r = O.forward(hb, np.zeros((1, 1), dtype=np.float32), 1, lambda e: ew, "mxfp4", "fp8")
+    s = frac_to_f32(Fraction(1, 448))                # token scale = amax/448
+    assert float(r["token_scales"][0]) == s
+    assert np.all(r["token_codes"] == 0x7E)          # 1/s rounds to 448
+    g = frac_to_f32(Fraction(448 * 32) * Fraction(0.5) * Fraction(s))
+    u = frac_to_f32(Fraction(448 * 32) * Fraction(0.25) * Fraction(s))
+    hv = float(np.float32(g / (1.0 + math.exp(-g)) * u))
+    exp_h = np.full(i, hv, dtype=np.float32)
+    exp_h[0] = -hv
+    assert np.array_equal(r["h"][0], exp_h)
+    s2 = frac_to_f32(Fraction(hv) / 448)
+    assert float(r["fc2_scales"][0]) == s2
+    assert r["fc2_codes"][0, 0] == 0xFE and np.all(r["fc2_codes"][0, 1:] == 0x7E)
+    acc_even = Fraction(448 * 30)                    # 31 positive, 1 negative
+    y_even = frac_to_f32(acc_even * Fraction(s2))
+    y_odd = frac_to_f32(acc_even / 2 * Fraction(s2))
+    exp_y = np.where(np.arange(h) % 2 == 0, y_even, y_odd).astype(np.float32)
+    assert np.array_equal(r["y2"][0], exp_y)
+    assert np.array_equal(r["out"][0], F.bf16_rne(exp_y))
+
+
+@pytest.mark.parametrize("wfmt,afmt", [("mxfp4", "fp8"), ("mxfp4", "bf16"), ("int4", "fp8")])
+def test_single_expert_equals_independent_mlp(wfmt, afmt):
+    """E = 1, k = 1: out = bf16(MLP(x)) computed here with torch float64 ops on
+    the decoded operands (an independent composition of the steps)."""
+    wl = MI.small_workload(tokens=9, experts=1, top_k=1, hidden=256, inter=128,
+                           wfmt=wfmt, afmt=afmt, seed=21)
+    hb = MI.hidden_bf16(wl.seed, wl.tokens, wl.hidden)
+    lg = MI.router_logits(wl.seed, wl.tokens, 1)
+    ex = _make_experts(wl.seed, 1, wl.hidden, wl.inter, wfmt)[0]
+    r = O.forward(hb, lg, 1, lambda e: ex, wfmt, afmt)
+    assert np.all(r["weights"] == 1.0)
+    x = torch.from_numpy(F.bf16_to_f32(hb).copy())
+    if afmt == "fp8":
+        amax = x.abs().amax(dim=1)
+        s = amax / 448.0                             # float32 tensor division
+        a = torch.from_numpy(F.e4m3_decode(F.e4m3_encode((x / s[:, None]).numpy())))
+    else:
+        s = torch.ones(wl.tokens)
+        a = x.double()
+    w1 = torch.from_numpy(O.layer.decode_weight(ex.w1q, ex.w1s, wfmt))
+    w2 = torch.from_numpy(O.layer.decode_weight(ex.w2q, ex.w2s, wfmt))
+    y1 = (torch.matmul(a, w1.t()) * s.double()[:, None]).float()
+    g, u = y1[:, :wl.inter].double(), y1[:, wl.inter:].double()
+    hh = (torch.nn.functional.silu(g) * u).float()
+    if afmt == "fp8":
+        s2 = hh.abs().amax(dim=1) / 448.0
+        a2 = torch.from_numpy(F.e4m3_decode(F.e4m3_encode((hh / s2[:, None]).numpy())))
+    else:
+        s2 = torch.ones(wl.tokens)
+        a2 = hh.to(torch.bfloat16).double()
+    y2 = (torch.matmul(a2, w2.t()) * s2.double()[:, None]).float()
+    ref = y2.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    # torch's silu may differ from exp-based silu by an ulp -> allow 1 bf16 ulp
+    diff = np.abs(r["out"].astype(np.int64) - ref.astype(np.int64))
+    assert diff.max() <= 1 and np.mean(diff == 0) > 0.97
+
+
+def test_identical_experts_reduce_to_one_expert():
+    wl = MI.small_workload(tokens=12, experts=5, top_k=3, hidden=128, inter=128, seed=8)
+    hb = MI.hidden_bf16(wl.seed, wl.tokens, wl.hidden)
+    lg = MI.router_logits(wl.seed, wl.tokens, wl.experts)
+    ex = _make_experts(wl.seed, 1, wl.hidden, wl.inter, "mxfp4")[0]
+    many = O.forward(hb, lg, 3, lambda e: ex, "mxfp4", "fp8")
+    one = O.forward(hb, lg[:, :1], 1, lambda e: ex, "mxfp4", "fp8")
+    assert np.array_equal(one["out"], F.bf16_rne(one["y2"][one["slot_row"][:, 0]]))
+    a = F.bf16_to_f32(many["out"]).astype(np.float64)
+    b = F.bf16_to_f32(one["out"]).astype(np.float64)
+    assert np.all(np.abs(a - b) <= np.abs(b) * 2.0 ** -7 + 1e-30)
+
+
+def test_per_token_independence_and_empty():
+    wl = MI.small_workload(tokens=20, experts=6, top_k=2, hidden=128, inter=128, seed=31)
+    hb = MI.hidden_bf16(wl.seed, wl.tokens, wl.hidden)
+    lg = MI.router_logits(wl.seed, wl.tokens, wl.experts, bias_sigma=2.0)
+    ex = _make_experts(wl.seed, wl.experts, wl.hidden, wl.inter, "mxfp4")
+    full = O.forward(hb, lg, 2, lambda e: ex[e], "mxfp4", "fp8")
+    sub = [3, 7, 19]
+    part = O.forward(hb[sub], lg[sub], 2, lambda e: ex[e], "mxfp4", "fp8")
+    assert np.array_equal(part["out"], full["out"][sub])
+    empty = O.forward(hb[:0], lg[:0], 2, lambda e: ex[e], "mxfp4", "fp8")
+    assert empty["out"].shape == (0, wl.hidden)
