@@ -1,0 +1,170 @@
+/*
+ * C ABI of the MI355X (gfx950) fused mixed-precision Mixture-of-Experts layer.
+ *
+ * The layer (flashinfer PR #3738, "perf: optimize MXFP4xBF16 & INT4xFP8 and add
+ * MXFP4xFP8 CUTLASS MoE backend for SM90", Description and Implementation
+ * Notes; flashinfer PR #4793, "Unify MoE CuTe DSL dispatch to be dtype
+ * agnostic", for the routing outputs and the finalize fusion):
+ *
+ *   1. top-k routing on float32 logits: the k largest logits per token (equal
+ *      logits ordered by the smaller expert index), weights = softmax over the
+ *      k selected logits;
+ *   2. FP8 activations: per-token E4M3 quantisation, s = amax/448, codes of
+ *      x/s rounded to nearest even and saturated at 448; BF16 activations are
+ *      used as they are;
+ *   3. grouped GEMM1 (gate+up) over the routed rows of each expert, times the
+ *      token scale, then h = silu(gate) * up in float32;
+ *   4. FC2 input: FP8 activations -> per-row E4M3 of h (same quantiser);
+ *      BF16 activations -> bf16(h);
+ *   5. grouped GEMM2, times the row scale (float32 y2);
+ *   6. out[t] = bf16(sum over the k slots of weight * y2), float32 sum.
+ *
+ * Weight formats: MXFP4 (E2M1 codes, one E8M0 scale per 32 elements along K)
+ * or INT4 (symmetric codes, one float32 scale per 128 elements along K).
+ * Supported combinations: MXFP4 x FP8, MXFP4 x BF16, INT4 x FP8.
+ *
+ * Conventions
+ *   - All tensors are dense row-major; "device" pointers are HIP device
+ *     memory on the current device; the caller owns every buffer.
+ *   - Every call is asynchronous on `stream` unless stated; no call
+ *     synchronises the stream or allocates, except moe_run (see below).
+ *   - Errors are returned as moe_status; moe_last_error() gives a message
+ *     for the calling thread.  Nothing is printed and nothing aborts.
+ *   - Asynchronous device faults surface at the caller's next
+ *     synchronisation.  With the environment variable MOE_SYNC_CHECK=1 every
+ *     call synchronises and checks each kernel, so a fault names its kernel.
+ *   - Pointers must be 16-byte aligned; hidden and inter must be multiples of
+ *     128; 1 <= num_experts <= 1024; 1 <= top_k <= min(num_experts, 16).
+ *   - Only gfx950 devices are supported (MOE_ERR_UNSUPPORTED otherwise).
+ */
+#ifndef MOE_AMD_MOE_H_
+#define MOE_AMD_MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* bad dims, pointers, alignment or ranges */
+  MOE_ERR_UNSUPPORTED = 2, /* format combination or device not supported */
+  MOE_ERR_WORKSPACE = 3,   /* caller workspace smaller than moe_workspace_query */
+  MOE_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_INTERNAL = 5
+} moe_status;
+
+typedef enum { MOE_W_MXFP4 = 0, MOE_W_INT4_G128 = 1 } moe_wfmt;
+typedef enum { MOE_A_FP8_TOKEN = 0, MOE_A_BF16 = 1 } moe_afmt;
+
+/* Shape and formats of one MoE layer.  W1 is [2*inter, hidden] per expert
+ * (rows [0, inter) gate, [inter, 2*inter) up); W2 is [hidden, inter]. */
+typedef struct {
+  int32_t num_experts;
+  int32_t hidden;
+  int32_t inter;
+  int32_t wfmt; /* moe_wfmt */
+  int32_t afmt; /* moe_afmt */
+} moe_dims;
+
+/* Byte offsets of the intermediates inside a moe_run_ws workspace (for
+ * inspection by tests; all regions are 256-byte aligned).
+ *   ids         int32  [T, k]   selected experts, descending logit
+ *   topk_w      float  [T, k]   routing weights
+ *   offsets     int32  [E + 1]  first expanded row of each expert
+ *   row_token   int32  [T*k]    token of each expanded row (expert-major,
+ *                               then token, then slot)
+ *   slot_row    int32  [T, k]   expanded row of each (token, slot)
+ *   tok_codes   uint8  [T, H]   E4M3 token codes (FP8 activations only)
+ *   tok_scales  float  [T]      token scales (FP8 activations only)
+ *   h           float  [T*k, I] SwiGLU output per expanded row
+ *   fc2_codes   uint8  [T*k, I] E4M3 (FP8) or bf16 bits ([T*k, I] uint16)
+ *   fc2_scales  float  [T*k]    per-row FC2 input scale (1.0 for BF16)
+ *   y2          float  [T*k, H] GEMM2 output per expanded row
+ *   num_tiles   int32  [1]      GEMM work-map length; tile_m rows per tile */
+typedef struct {
+  size_t total;
+  size_t ids, topk_w, chunk_counts, offsets, row_token, slot_row, tiles, num_tiles;
+  size_t tok_codes, tok_scales, h, fc2_codes, fc2_scales, y2;
+  int32_t tile_m;
+  int32_t gemm_cfg;
+  int64_t max_tiles;
+} moe_ws_layout;
+
+int32_t moe_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Bytes of the packed weights and of the scales for all experts (pure host
+ * arithmetic).  Per expert: codes (2*I*H + H*I)/2 bytes; scales
+ * 2*I*ceil(H/512)*16 + H*ceil(I/512)*16 bytes (MXFP4) or
+ * 4*(2*I*H + H*I)/128 bytes (INT4). */
+moe_status moe_weights_query(const moe_dims* dims, size_t* weight_bytes, size_t* scale_bytes);
+
+/* Quantises float32 master weights of experts [expert_begin, expert_begin +
+ * expert_count) into the device layout.
+ *   w1: device float [expert_count, 2*inter, hidden]
+ *   w2: device float [expert_count, hidden, inter]
+ *   weights, scales: device buffers of moe_weights_query's sizes (all experts);
+ *   only the slice of the given experts is written.
+ * Quantisation (MXFP4: shared exponent floor(log2(block amax)) - 2, elements
+ * rounded to nearest even on the E2M1 grid and clamped to +-6; INT4: scale
+ * amax/7, codes round-half-even(w/s)) is deterministic and stream-ordered.
+ * Call it repeatedly over expert chunks so that the float32 masters never
+ * need to be resident at once. */
+moe_status moe_prepare_weights(const moe_dims* dims, const float* w1, const float* w2,
+                               int32_t expert_begin, int32_t expert_count, void* weights,
+                               void* scales, hipStream_t stream);
+
+/* Inverse of the device layout, for checking codes bit for bit: writes the
+ * canonical row-major codes and scales of experts [expert_begin,
+ * expert_begin + expert_count) into device buffers
+ *   w1q uint8 [n, 2*inter, hidden/2]   (element 2i in the low nibble;
+ *                                        INT4 as two's complement)
+ *   w1s uint8 [n, 2*inter, hidden/32]  (MXFP4 E8M0) or float [n, 2*inter, hidden/128] (INT4)
+ *   w2q uint8 [n, hidden, inter/2]
+ *   w2s uint8 [n, hidden, inter/32]    or float [n, hidden, inter/128]. */
+moe_status moe_unpack_weights(const moe_dims* dims, const void* weights, const void* scales,
+                              int32_t expert_begin, int32_t expert_count, void* w1q, void* w1s,
+                              void* w2q, void* w2s, hipStream_t stream);
+
+/* Workspace bytes moe_run_ws needs for num_tokens tokens and top_k. */
+moe_status moe_workspace_query(const moe_dims* dims, int64_t num_tokens, int32_t top_k,
+                               size_t* bytes);
+
+/* Offsets of the intermediates inside that workspace. */
+moe_status moe_workspace_layout(const moe_dims* dims, int64_t num_tokens, int32_t top_k,
+                                moe_ws_layout* layout);
+
+/* Runs the layer with a caller-owned workspace.
+ *   hidden:        device bf16 bits [num_tokens, hidden]
+ *   router_logits: device float [num_tokens, num_experts] (finite values)
+ *   weights, scales: prepared by moe_prepare_weights for all experts
+ *   out:           device bf16 bits [num_tokens, hidden], fully overwritten
+ *   workspace:     device buffer of at least moe_workspace_query bytes
+ * num_tokens = 0 returns MOE_OK without launching.  No allocation and no
+ * host synchronisation (unless MOE_SYNC_CHECK=1). */
+moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_tokens,
+                      const float* router_logits, const void* weights, const void* scales,
+                      int32_t top_k, void* out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Same as moe_run_ws, with a workspace the library keeps per (device,
+ * stream) and grows stream-ordered (hipMallocAsync) when a call needs more.
+ * Calls on different streams use different workspaces. */
+moe_status moe_run(const moe_dims* dims, const void* hidden, int64_t num_tokens,
+                   const float* router_logits, const void* weights, const void* scales,
+                   int32_t top_k, void* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_AMD_MOE_H_ */

@@ -1,0 +1,160 @@
+"""Python binding of the MI355X fused mixed-precision MoE library (libmoe_amd.so).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+the library; PyTorch provides device memory and the current stream.  The C
+ABI is declared in include/moe.h.  If the library is missing every call raises
+(there is no CPU fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_amd.so")
+
+W_MXFP4, W_INT4_G128 = 0, 1
+A_FP8_TOKEN, A_BF16 = 0, 1
+WFMT = {"mxfp4": W_MXFP4, "int4": W_INT4_G128}
+AFMT = {"fp8": A_FP8_TOKEN, "bf16": A_BF16}
+
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
+          3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP", 5: "MOE_ERR_INTERNAL"}
+
+EXPORTS = ("moe_abi_version", "moe_last_error", "moe_weights_query", "moe_prepare_weights",
+           "moe_unpack_weights", "moe_workspace_query", "moe_workspace_layout", "moe_run_ws",
+           "moe_run")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("inter", ctypes.c_int32), ("wfmt", ctypes.c_int32), ("afmt", ctypes.c_int32)]
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "total", "ids", "topk_w", "chunk_counts", "offsets", "row_token", "slot_row", "tiles",
+        "num_tiles", "tok_codes", "tok_scales", "h", "fc2_codes", "fc2_scales", "y2")] + [
+        ("tile_m", ctypes.c_int32), ("gemm_cfg", ctypes.c_int32), ("max_tiles", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mixed_precision_moe_topk_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        DP = ctypes.POINTER(Dims)
+        L.moe_abi_version.restype = I32
+        L.moe_last_error.restype = ctypes.c_char_p
+        sig = {
+            "moe_weights_query": [DP, ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
+            "moe_prepare_weights": [DP, P, P, I32, I32, P, P, P],
+            "moe_unpack_weights": [DP, P, P, I32, I32, P, P, P, P, P],
+            "moe_workspace_query": [DP, I64, I32, ctypes.POINTER(SZ)],
+            "moe_workspace_layout": [DP, I64, I32, ctypes.POINTER(WsLayout)],
+            "moe_run_ws": [DP, P, I64, P, P, P, I32, P, P, SZ, P],
+            "moe_run": [DP, P, I64, P, P, P, I32, P, P],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+@dataclass(frozen=True)
+class LayerDims:
+    num_experts: int
+    hidden: int
+    inter: int
+    wfmt: str = "mxfp4"
+    afmt: str = "fp8"
+
+    def c(self) -> Dims:
+        return Dims(self.num_experts, self.hidden, self.inter, WFMT[self.wfmt], AFMT[self.afmt])
+
+
+def abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def weights_query(d: LayerDims):
+    w, s = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().moe_weights_query(ctypes.byref(d.c()), ctypes.byref(w), ctypes.byref(s)))
+    return w.value, s.value
+
+
+def prepare_weights(d: LayerDims, w1, w2, expert_begin: int, weights, scales, stream=None):
+    """w1: float32 cuda [n, 2I, H]; w2: float32 cuda [n, H, I] for experts
+    [expert_begin, expert_begin + n); weights/scales: uint8 cuda buffers."""
+    n = 0 if w1 is None else int(w1.shape[0])
+    _check(lib().moe_prepare_weights(ctypes.byref(d.c()), _ptr(w1), _ptr(w2), expert_begin, n,
+                                     _ptr(weights), _ptr(scales), _stream(stream)))
+
+
+def unpack_weights(d: LayerDims, weights, scales, expert_begin: int, w1q, w1s, w2q, w2s,
+                   stream=None):
+    n = int(w1q.shape[0])
+    _check(lib().moe_unpack_weights(ctypes.byref(d.c()), _ptr(weights), _ptr(scales),
+                                    expert_begin, n, _ptr(w1q), _ptr(w1s), _ptr(w2q), _ptr(w2s),
+                                    _stream(stream)))
+
+
+def workspace_query(d: LayerDims, num_tokens: int, top_k: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().moe_workspace_query(ctypes.byref(d.c()), num_tokens, top_k, ctypes.byref(b)))
+    return b.value
+
+
+def workspace_layout(d: LayerDims, num_tokens: int, top_k: int) -> WsLayout:
+    L = WsLayout()
+    _check(lib().moe_workspace_layout(ctypes.byref(d.c()), num_tokens, top_k, ctypes.byref(L)))
+    return L
+
+
+def run_ws(d: LayerDims, hidden, logits, weights, scales, top_k: int, out, workspace,
+           stream=None):
+    """hidden: bf16 (or int16 bits) cuda [T, H]; logits: float32 cuda [T, E];
+    out: bf16 cuda [T, H]; workspace: uint8 cuda of workspace_query bytes."""
+    T = int(hidden.shape[0])
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().moe_run_ws(ctypes.byref(d.c()), _ptr(hidden), T, _ptr(logits), _ptr(weights),
+                            _ptr(scales), top_k, _ptr(out), _ptr(workspace), nbytes,
+                            _stream(stream)))
+
+
+def run(d: LayerDims, hidden, logits, weights, scales, top_k: int, out, stream=None):
+    T = int(hidden.shape[0])
+    _check(lib().moe_run(ctypes.byref(d.c()), _ptr(hidden), T, _ptr(logits), _ptr(weights),
+                         _ptr(scales), top_k, _ptr(out), _stream(stream)))

@@ -1,0 +1,431 @@
+// Host side of the C ABI declared in include/moe.h: validation, size queries,
+// workspace carving and the launch sequence of one MoE layer on one stream.
+//
+// Validation rules follow the review findings on flashinfer PR #3738 ("perf:
+// optimize MXFP4xBF16 & INT4xFP8 and add MXFP4xFP8 CUTLASS MoE backend for
+// SM90"): shape preconditions are checked before any launch, sub-byte weight
+// offsets are computed in bytes (elements / 2), work indices are 64-bit, and an
+// empty routed batch is a no-op.  The caller-owned workspace mirrors the
+// workspace-size query of flashinfer's fused MoE (PR #4411 page, "revert(moe):
+// revert #3738 ...", Conflict resolution: caller-owned workspace kept).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/moe.h"
+#include "moe_common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moe_status ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+bool sync_check_enabled() {
+  static const bool on = [] {
+    const char* v = getenv("MOE_SYNC_CHECK");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+moe_status hip_check(hipError_t e, const char* what, hipStream_t st) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  if (sync_check_enabled()) {
+    e = hipStreamSynchronize(st);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s (synchronised check): %s", what,
+                                     hipGetErrorString(e));
+  }
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)                 \
+  do {                                \
+    moe_status _s = (expr);           \
+    if (_s != MOE_OK) return _s;      \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+moe_status check_dims(const moe_dims* d) {
+  if (!d) return fail(MOE_ERR_INVALID_ARG, "dims is null");
+  if (d->num_experts < 1 || d->num_experts > moe::kMaxExperts)
+    return fail(MOE_ERR_INVALID_ARG, "num_experts %d outside [1, %d]", d->num_experts,
+                moe::kMaxExperts);
+  if (d->hidden < 128 || d->hidden % 128 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "hidden %d must be a positive multiple of 128", d->hidden);
+  if (d->inter < 128 || d->inter % 128 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "inter %d must be a positive multiple of 128", d->inter);
+  if (d->wfmt != MOE_W_MXFP4 && d->wfmt != MOE_W_INT4_G128)
+    return fail(MOE_ERR_INVALID_ARG, "unknown weight format %d", d->wfmt);
+  if (d->afmt != MOE_A_FP8_TOKEN && d->afmt != MOE_A_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown activation format %d", d->afmt);
+  if (d->wfmt == MOE_W_INT4_G128 && d->afmt == MOE_A_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "INT4 weights with BF16 activations are not supported");
+  return MOE_OK;
+}
+
+struct Sizes {
+  int64_t w1_codes, w2_codes, codes_per_expert;
+  int64_t w1_scales, w2_scales, scales_per_expert;
+};
+
+Sizes sizes_of(const moe_dims* d) {
+  Sizes s;
+  const int64_t H = d->hidden, I = d->inter;
+  s.w1_codes = 2 * I * H / 2;
+  s.w2_codes = H * I / 2;
+  s.codes_per_expert = s.w1_codes + s.w2_codes;
+  if (d->wfmt == MOE_W_MXFP4) {
+    s.w1_scales = (2 * I / 16) * cdiv(H / 128, 4) * 256;
+    s.w2_scales = (H / 16) * cdiv(I / 128, 4) * 256;
+  } else {
+    s.w1_scales = 2 * I * (H / 128) * 4;
+    s.w2_scales = H * (I / 128) * 4;
+  }
+  s.scales_per_expert = s.w1_scales + s.w2_scales;
+  return s;
+}
+
+int variant_of(const moe_dims* d) {
+  if (d->wfmt == MOE_W_INT4_G128) return moe::kInt4Fp8;
+  return d->afmt == MOE_A_BF16 ? moe::kMxfp4Bf16 : moe::kMxfp4Fp8;
+}
+
+// GEMM tile shape from the mean rows per expert.
+int pick_cfg(int64_t rows, int32_t experts) {
+  const double avg = (double)rows / (double)experts;
+  if (avg <= 16.0) return 0;
+  if (avg <= 48.0) return 1;
+  return 2;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+moe_status layout_of(const moe_dims* d, int64_t T, int32_t k, moe_ws_layout* L) {
+  MOE_TRY(check_dims(d));
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "num_tokens %lld < 0", (long long)T);
+  if (k < 1 || k > moe::kMaxTopK || k > d->num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "top_k %d outside [1, min(num_experts, %d)]", k,
+                moe::kMaxTopK);
+  const int64_t rows = T * k;
+  if (T > (int64_t)1 << 26 || rows >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_INVALID_ARG, "num_tokens %lld too large", (long long)T);
+  const int64_t E = d->num_experts, H = d->hidden, I = d->inter;
+  const int cfg = pick_cfg(rows, d->num_experts);
+  const int tile_m = moe::gemm_cfg(cfg).bm();
+  const int64_t nchunks = cdiv(rows, moe::kRouteChunk);
+  const int64_t max_tiles = cdiv(rows, tile_m) + std::min<int64_t>(E, rows);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  std::memset(L, 0, sizeof(*L));
+  L->ids = take(rows * 4);
+  L->topk_w = take(rows * 4);
+  L->chunk_counts = take(nchunks * E * 4);
+  L->offsets = take((E + 1) * 4);
+  L->row_token = take(rows * 4);
+  L->slot_row = take(rows * 4);
+  L->tiles = take(max_tiles * sizeof(moe::Tile));
+  L->num_tiles = take(4);
+  const bool fp8 = d->afmt == MOE_A_FP8_TOKEN;
+  L->tok_codes = take(fp8 ? T * H : 0);
+  L->tok_scales = take(fp8 ? T * 4 : 0);
+  L->h = take(rows * I * 4);
+  L->fc2_codes = take(rows * I * (fp8 ? 1 : 2));
+  L->fc2_scales = take(rows * 4);
+  L->y2 = take(rows * H * 4);
+  L->total = off;
+  L->tile_m = tile_m;
+  L->gemm_cfg = cfg;
+  L->max_tiles = max_tiles;
+  return MOE_OK;
+}
+
+// gfx950 check, cached per device.
+moe_status check_device() {
+  static std::mutex mu;
+  static std::map<int, bool> known;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = known.find(dev);
+  if (it == known.end()) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(MOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    const bool good = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    it = known.emplace(dev, good).first;
+  }
+  if (!it->second) return fail(MOE_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_weights_query(const moe_dims* dims, size_t* weight_bytes, size_t* scale_bytes) {
+  MOE_TRY(check_dims(dims));
+  if (!weight_bytes || !scale_bytes) return fail(MOE_ERR_INVALID_ARG, "null output pointer");
+  const Sizes s = sizes_of(dims);
+  *weight_bytes = (size_t)(s.codes_per_expert * dims->num_experts);
+  *scale_bytes = (size_t)(s.scales_per_expert * dims->num_experts);
+  return ok();
+}
+
+moe_status moe_prepare_weights(const moe_dims* dims, const float* w1, const float* w2,
+                               int32_t expert_begin, int32_t expert_count, void* weights,
+                               void* scales, hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  if (expert_begin < 0 || expert_count < 0 ||
+      (int64_t)expert_begin + expert_count > dims->num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "expert slice [%d, %d+%d) outside [0, %d)", expert_begin,
+                expert_begin, expert_count, dims->num_experts);
+  if (expert_count == 0) return ok();
+  if (!w1 || !w2 || !weights || !scales)
+    return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(w1) || !aligned16(w2) || !aligned16(weights) || !aligned16(scales))
+    return fail(MOE_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  MOE_TRY(check_device());
+  const Sizes s = sizes_of(dims);
+  const int int4 = dims->wfmt == MOE_W_INT4_G128;
+  const int32_t H = dims->hidden, I = dims->inter;
+  uint8_t* cw = static_cast<uint8_t*>(weights) + (int64_t)expert_begin * s.codes_per_expert;
+  uint8_t* cs = static_cast<uint8_t*>(scales) + (int64_t)expert_begin * s.scales_per_expert;
+  if (!int4)  // unused scale bytes (K/128 not a multiple of 4) read as 1.0
+    MOE_TRY(hip_check(hipMemsetAsync(cs, 0x7F, (size_t)(s.scales_per_expert * expert_count),
+                                     stream), "hipMemsetAsync(scales)", stream));
+  MOE_TRY(hip_check(moe::launch_prepare(int4, w1, expert_count, 2 * I, H, true, cw,
+                                        s.codes_per_expert, cs, s.scales_per_expert, stream),
+                    "prepare W1", stream));
+  MOE_TRY(hip_check(moe::launch_prepare(int4, w2, expert_count, H, I, false, cw + s.w1_codes,
+                                        s.codes_per_expert, cs + s.w1_scales,
+                                        s.scales_per_expert, stream),
+                    "prepare W2", stream));
+  return ok();
+}
+
+moe_status moe_unpack_weights(const moe_dims* dims, const void* weights, const void* scales,
+                              int32_t expert_begin, int32_t expert_count, void* w1q, void* w1s,
+                              void* w2q, void* w2s, hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  if (expert_begin < 0 || expert_count < 0 ||
+      (int64_t)expert_begin + expert_count > dims->num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "expert slice outside [0, %d)", dims->num_experts);
+  if (expert_count == 0) return ok();
+  if (!weights || !scales || !w1q || !w1s || !w2q || !w2s)
+    return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(weights) || !aligned16(scales) || !aligned16(w1q) || !aligned16(w2q) ||
+      !aligned16(w1s) || !aligned16(w2s))
+    return fail(MOE_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  MOE_TRY(check_device());
+  const Sizes s = sizes_of(dims);
+  const int int4 = dims->wfmt == MOE_W_INT4_G128;
+  const int32_t H = dims->hidden, I = dims->inter;
+  const uint8_t* cw = static_cast<const uint8_t*>(weights) + (int64_t)expert_begin * s.codes_per_expert;
+  const uint8_t* cs = static_cast<const uint8_t*>(scales) + (int64_t)expert_begin * s.scales_per_expert;
+  MOE_TRY(hip_check(moe::launch_unpack(int4, cw, s.codes_per_expert, cs, s.scales_per_expert,
+                                       expert_count, 2 * I, H, true,
+                                       static_cast<uint8_t*>(w1q), static_cast<uint8_t*>(w1s),
+                                       stream), "unpack W1", stream));
+  MOE_TRY(hip_check(moe::launch_unpack(int4, cw + s.w1_codes, s.codes_per_expert,
+                                       cs + s.w1_scales, s.scales_per_expert, expert_count, H, I,
+                                       false, static_cast<uint8_t*>(w2q),
+                                       static_cast<uint8_t*>(w2s), stream), "unpack W2", stream));
+  return ok();
+}
+
+moe_status moe_workspace_query(const moe_dims* dims, int64_t num_tokens, int32_t top_k,
+                               size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "null output pointer");
+  moe_ws_layout L;
+  MOE_TRY(layout_of(dims, num_tokens, top_k, &L));
+  *bytes = L.total;
+  return ok();
+}
+
+moe_status moe_workspace_layout(const moe_dims* dims, int64_t num_tokens, int32_t top_k,
+                                moe_ws_layout* layout) {
+  if (!layout) return fail(MOE_ERR_INVALID_ARG, "null output pointer");
+  MOE_TRY(layout_of(dims, num_tokens, top_k, layout));
+  return ok();
+}
+
+moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_tokens,
+                      const float* router_logits, const void* weights, const void* scales,
+                      int32_t top_k, void* out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  moe_ws_layout L;
+  MOE_TRY(layout_of(dims, num_tokens, top_k, &L));
+  if (num_tokens == 0) return ok();
+  if (!hidden || !router_logits || !weights || !scales || !out || !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(hidden) || !aligned16(router_logits) || !aligned16(weights) ||
+      !aligned16(scales) || !aligned16(out) || !aligned16(workspace))
+    return fail(MOE_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes,
+                L.total);
+  MOE_TRY(check_device());
+
+  const Sizes s = sizes_of(dims);
+  const int64_t T = num_tokens, rows = T * top_k;
+  const int32_t E = dims->num_experts, H = dims->hidden, I = dims->inter;
+  const bool fp8 = dims->afmt == MOE_A_FP8_TOKEN;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+
+  moe::RouteParams rp;
+  rp.logits = router_logits;
+  rp.tokens = T;
+  rp.experts = E;
+  rp.top_k = top_k;
+  rp.ids = reinterpret_cast<int32_t*>(ws + L.ids);
+  rp.weights = reinterpret_cast<float*>(ws + L.topk_w);
+  rp.chunk_counts = reinterpret_cast<int32_t*>(ws + L.chunk_counts);
+  rp.nchunks = (int32_t)cdiv(rows, moe::kRouteChunk);
+  rp.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  rp.row_token = reinterpret_cast<int32_t*>(ws + L.row_token);
+  rp.slot_row = reinterpret_cast<int32_t*>(ws + L.slot_row);
+  rp.tiles = reinterpret_cast<moe::Tile*>(ws + L.tiles);
+  rp.num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
+  rp.tile_m = L.tile_m;
+  MOE_TRY(hip_check(moe::launch_route(rp, stream), "route", stream));
+
+  const float* tok_scales = nullptr;
+  const uint8_t* a1 = static_cast<const uint8_t*>(hidden);
+  int64_t a1_stride = (int64_t)H * 2;
+  if (fp8) {
+    uint8_t* codes = ws + L.tok_codes;
+    float* sc = reinterpret_cast<float*>(ws + L.tok_scales);
+    MOE_TRY(hip_check(moe::launch_quant_tokens(static_cast<const uint16_t*>(hidden), T, H,
+                                               codes, sc, stream), "quantize tokens", stream));
+    tok_scales = sc;
+    a1 = codes;
+    a1_stride = H;
+  }
+
+  const int variant = variant_of(dims);
+  const moe::GemmCfg cfg = moe::gemm_cfg(L.gemm_cfg);
+  const uint8_t* wbytes = static_cast<const uint8_t*>(weights);
+  const uint8_t* sbytes = static_cast<const uint8_t*>(scales);
+  float* h = reinterpret_cast<float*>(ws + L.h);
+
+  moe::GemmParams g1;
+  g1.a = a1;
+  g1.a_stride = a1_stride;
+  g1.row_token = rp.row_token;
+  g1.row_scale = tok_scales;
+  g1.w = wbytes;
+  g1.w_expert_stride = s.codes_per_expert;
+  g1.s = sbytes;
+  g1.s_expert_stride = s.scales_per_expert;
+  g1.tiles = rp.tiles;
+  g1.num_tiles = rp.num_tiles;
+  g1.K = H;
+  g1.N = 2 * I;
+  g1.n_tiles = (2 * I) / cfg.bn();
+  g1.out = h;
+  g1.out_stride = I;
+  MOE_TRY(hip_check(moe::launch_gemm(variant, true, L.gemm_cfg, g1, L.max_tiles, stream),
+                    "gemm1", stream));
+
+  uint8_t* q2 = ws + L.fc2_codes;
+  float* s2 = reinterpret_cast<float*>(ws + L.fc2_scales);
+  MOE_TRY(hip_check(moe::launch_requant(h, rows, I, fp8 ? 0 : 1, q2, s2, stream),
+                    "fc2 requant", stream));
+
+  float* y2 = reinterpret_cast<float*>(ws + L.y2);
+  moe::GemmParams g2;
+  g2.a = q2;
+  g2.a_stride = (int64_t)I * (fp8 ? 1 : 2);
+  g2.row_token = nullptr;
+  g2.row_scale = fp8 ? s2 : nullptr;
+  g2.w = wbytes + s.w1_codes;
+  g2.w_expert_stride = s.codes_per_expert;
+  g2.s = sbytes + s.w1_scales;
+  g2.s_expert_stride = s.scales_per_expert;
+  g2.tiles = rp.tiles;
+  g2.num_tiles = rp.num_tiles;
+  g2.K = I;
+  g2.N = H;
+  g2.n_tiles = H / cfg.bn();
+  g2.out = y2;
+  g2.out_stride = H;
+  MOE_TRY(hip_check(moe::launch_gemm(variant, false, L.gemm_cfg, g2, L.max_tiles, stream),
+                    "gemm2", stream));
+
+  MOE_TRY(hip_check(moe::launch_finalize(y2, rp.weights, rp.slot_row, T, top_k, H,
+                                         static_cast<uint16_t*>(out), stream),
+                    "finalize", stream));
+  return ok();
+}
+
+moe_status moe_run(const moe_dims* dims, const void* hidden, int64_t num_tokens,
+                   const float* router_logits, const void* weights, const void* scales,
+                   int32_t top_k, void* out, hipStream_t stream) {
+  moe_ws_layout L;
+  MOE_TRY(layout_of(dims, num_tokens, top_k, &L));
+  if (num_tokens == 0) return ok();
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> arenas;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  void* ws = nullptr;
+  size_t cap = 0;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto& slot = arenas[{dev, stream}];
+    if (slot.second < L.total) {
+      if (slot.first) {
+        e = hipFreeAsync(slot.first, stream);
+        if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipFreeAsync: %s", hipGetErrorString(e));
+        slot = {nullptr, 0};
+      }
+      void* p = nullptr;
+      e = hipMallocAsync(&p, L.total, stream);
+      if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipMallocAsync: %s", hipGetErrorString(e));
+      slot = {p, L.total};
+    }
+    ws = slot.first;
+    cap = slot.second;
+  }
+  return moe_run_ws(dims, hidden, num_tokens, router_logits, weights, scales, top_k, out, ws,
+                    cap, stream);
+}
+
+}  // extern "C"

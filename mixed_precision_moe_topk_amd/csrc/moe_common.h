@@ -1,0 +1,161 @@
+// Shared device helpers and launch-parameter structs of the fused MoE library
+// (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- constants
+constexpr int kWave = 64;
+constexpr int kKStep = 128;        // K consumed by one 16x16x128 MFMA
+constexpr int kMxBlock = 32;       // elements per E8M0 scale (OCP MX block)
+constexpr int kInt4Group = 128;    // elements per INT4 group scale
+constexpr int kRouteChunk = 1024;  // (token, slot) pairs per routing chunk
+constexpr int kMaxTopK = 16;
+constexpr int kMaxExperts = 1024;
+
+enum Variant : int {
+  kMxfp4Fp8 = 0,   // E2M1 weights (E8M0 / 32) x per-token E4M3 activations
+  kMxfp4Bf16 = 1,  // E2M1 weights (E8M0 / 32) x bf16 activations
+  kInt4Fp8 = 2,    // INT4 weights (fp32 / 128) x per-token E4M3 activations
+};
+
+// Work item of the grouped GEMMs: rows [row0, row0 + nrows) of expert `expert`.
+struct Tile {
+  int32_t expert;
+  int32_t row0;
+  int32_t nrows;
+  int32_t pad;
+};
+
+// ---------------------------------------------------------------- vectors
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- numerics
+// Round a finite float to the nearest OCP E4M3 ("FN") code: ties to even
+// mantissa, magnitudes above 448 saturate to 448, the sign is kept when the
+// magnitude rounds to zero.  Integer bit manipulation on the float32 pattern.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    // below the smallest normal 2^-6 the codes are multiples of 2^-9; 8 is 0x08
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b += 0x7FFFFu + ((b >> 20) & 1u);  // round to 3 mantissa bits, ties to even
+    code = (b >> 20) - (120u << 3);    // exponent bias 127 -> 7
+  }
+  return sign | code;
+}
+
+// float32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits(float v) {
+  uint32_t b = __float_as_uint(v);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+
+__device__ __forceinline__ float e8m0_to_float(uint32_t c) {
+  // 2^(c-127); c = 0 is the float32 subnormal 2^-127
+  return __uint_as_float(c ? (c << 23) : 0x00400000u);
+}
+
+// E4M3 codes of the magnitudes 0..7 (byte j of the 8-byte table {hi:lo}):
+//   0:00 1:38 2:40 3:44 4:48 5:4A 6:4C 7:4E.  Every INT4 value is exact in
+// E4M3; the sign is bit 7 of the code.
+constexpr uint32_t kI4MagLo = 0x44403800u, kI4MagHi = 0x4E4C4A48u;
+
+// Four sign-magnitude INT4 nibbles, one per byte (bits 0-2 magnitude, bit 3
+// sign, bits 4-7 zero) -> four E4M3 codes.
+__device__ __forceinline__ uint32_t int4sm_to_e4m3(uint32_t nib4) {
+  const uint32_t mag = __builtin_amdgcn_perm(kI4MagHi, kI4MagLo, nib4 & 0x07070707u);
+  return mag | ((nib4 & 0x08080808u) << 4);
+}
+
+// ---------------------------------------------------------------- wave ops
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// ---------------------------------------------------------------- params
+struct RouteParams {
+  const float* logits;     // [T, E]
+  int64_t tokens;
+  int32_t experts;
+  int32_t top_k;
+  int32_t* ids;            // [T, k]
+  float* weights;          // [T, k]
+  int32_t* chunk_counts;   // [nchunks, E]
+  int32_t nchunks;
+  int32_t* offsets;        // [E + 1]
+  int32_t* row_token;      // [T*k]
+  int32_t* slot_row;       // [T*k]
+  Tile* tiles;             // [max_tiles]
+  int32_t* num_tiles;      // [1]
+  int32_t tile_m;
+};
+
+struct GemmParams {
+  const uint8_t* a;            // FC1: token rows (E4M3 or bf16); FC2: expanded rows
+  int64_t a_stride;            // bytes per A row
+  const int32_t* row_token;    // FC1 gather map (expanded row -> token); null for FC2
+  const float* row_scale;      // FC1: per-token scale; FC2: per-row scale; null for bf16
+  const uint8_t* w;            // packed weights of expert 0 of this matrix
+  int64_t w_expert_stride;     // bytes between experts
+  const uint8_t* s;            // scales of expert 0 of this matrix
+  int64_t s_expert_stride;
+  const Tile* tiles;
+  const int32_t* num_tiles;
+  int32_t n_tiles;             // N / BN
+  int32_t K;
+  int32_t N;                   // device columns (FC1: 2I interleaved gate/up; FC2: H)
+  float* out;                  // FC1: h [rows, N/2]; FC2: y2 [rows, N]
+  int64_t out_stride;          // floats per output row
+};
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_route(const RouteParams& p, hipStream_t st);
+hipError_t launch_quant_tokens(const uint16_t* x, int64_t T, int32_t H, uint8_t* codes,
+                               float* scales, hipStream_t st);
+hipError_t launch_requant(const float* h, int64_t rows, int32_t I, int afmt_bf16,
+                          uint8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_finalize(const float* y2, const float* weights, const int32_t* slot_row,
+                           int64_t T, int32_t k, int32_t H, uint16_t* out, hipStream_t st);
+hipError_t launch_gemm(int variant, bool fc1, int cfg, const GemmParams& p, int64_t max_tiles,
+                       hipStream_t st);
+hipError_t launch_prepare(int wfmt_int4, const float* w, int32_t n_experts, int32_t N,
+                          int32_t K, bool interleave_gate_up, uint8_t* codes,
+                          int64_t codes_stride, uint8_t* scales, int64_t scales_stride,
+                          hipStream_t st);
+hipError_t launch_unpack(int wfmt_int4, const uint8_t* codes, int64_t codes_stride,
+                         const uint8_t* scales, int64_t scales_stride, int32_t n_experts,
+                         int32_t N, int32_t K, bool interleave_gate_up, uint8_t* out_codes,
+                         uint8_t* out_scales, hipStream_t st);
+
+// GEMM tile configurations (rows per block tile; columns per block tile).
+struct GemmCfg {
+  int waves_m, wm, wn;
+  int bm() const { return 16 * waves_m * wm; }
+  int bn() const { return 16 * (4 / waves_m) * wn; }
+};
+constexpr int kNumGemmCfg = 3;
+inline GemmCfg gemm_cfg(int i) {
+  switch (i) {
+    case 0: return GemmCfg{1, 1, 2};  // 16 x 128: decode-sized experts
+    case 1: return GemmCfg{1, 3, 2};  // 48 x 128
+    default: return GemmCfg{2, 4, 4}; // 128 x 128: prefill
+  }
+}
+
+}  // namespace moe

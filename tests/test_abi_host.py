@@ -1,0 +1,98 @@
+"""The C-ABI library loads, exports every symbol include/moe.h declares, and
+rejects bad arguments on the host before touching a device (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixed_precision_moe_topk_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|int32_t|const char\*)\s+(moe_\w+)\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(M.LIB_PATH):
+        pytest.skip("library not built")
+    return M.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) == set(M.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.moe_abi_version() == 1
+
+
+def _d(**kw):
+    base = dict(num_experts=256, hidden=7168, inter=2048, wfmt="mxfp4", afmt="fp8")
+    base.update(kw)
+    return M.LayerDims(**base)
+
+
+def test_weight_sizes(L):
+    w, s = M.weights_query(_d())
+    assert w == 256 * (2 * 2048 * 7168 + 7168 * 2048) // 2
+    assert s == 256 * (2 * 2048 * 7168 + 7168 * 2048) // 32
+    w, s = M.weights_query(_d(wfmt="int4"))
+    assert s == 256 * (2 * 2048 * 7168 + 7168 * 2048) // 128 * 4
+    # K/128 not a multiple of 4: scale rows are padded to 512-element chunks
+    w, s = M.weights_query(_d(num_experts=8, hidden=256, inter=512))
+    assert s == 8 * (1024 * 1 * 16 + 256 * 1 * 16)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=100), 1), (dict(inter=0), 1), (dict(num_experts=0), 1),
+    (dict(num_experts=2000), 1), (dict(wfmt="int4", afmt="bf16"), 2)])
+def test_bad_dims(L, kw, status):
+    with pytest.raises(M.MoeError) as ei:
+        M.weights_query(_d(**kw))
+    assert ei.value.status == status
+
+
+def test_bad_topk_and_tokens(L):
+    with pytest.raises(M.MoeError) as ei:
+        M.workspace_query(_d(num_experts=8), 16, 9)
+    assert ei.value.status == 1
+    with pytest.raises(M.MoeError):
+        M.workspace_query(_d(), 16, 17)
+    with pytest.raises(M.MoeError):
+        M.workspace_query(_d(), -1, 8)
+    assert M.workspace_query(_d(), 0, 8) > 0
+
+
+def test_run_rejects_before_launch(L):
+    d = _d(num_experts=8, hidden=256, inter=512).c()
+    P = ctypes.c_void_p
+    # T = 0 is a no-op success even with null pointers
+    assert L.moe_run_ws(ctypes.byref(d), None, 0, None, None, None, 2, None, None, 0, None) == 0
+    # null pointers
+    assert L.moe_run_ws(ctypes.byref(d), None, 4, None, None, None, 2, None, None, 0, None) == 1
+    # misaligned pointer
+    fake = P(0x1000 + 8)
+    ok = P(0x1000)
+    assert L.moe_run_ws(ctypes.byref(d), fake, 4, ok, ok, ok, 2, ok, ok, 1 << 30, None) == 1
+    # workspace too small
+    assert L.moe_run_ws(ctypes.byref(d), ok, 4, ok, ok, ok, 2, ok, ok, 16, None) == 3
+    assert b"workspace" in L.moe_last_error()
+    # expert slice out of range
+    assert L.moe_prepare_weights(ctypes.byref(d), ok, ok, 6, 3, ok, ok, None) == 1
+    assert L.moe_prepare_weights(ctypes.byref(d), ok, ok, 0, 0, ok, ok, None) == 0
+
+
+def test_workspace_layout_regions(L):
+    lay = M.workspace_layout(_d(), 4096, 8)
+    offs = [lay.ids, lay.topk_w, lay.chunk_counts, lay.offsets, lay.row_token, lay.slot_row,
+            lay.tiles, lay.num_tiles, lay.tok_codes, lay.tok_scales, lay.h, lay.fc2_codes,
+            lay.fc2_scales, lay.y2]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.y2 + 4096 * 8 * 7168 * 4 <= lay.total
+    assert lay.tile_m == 128 and lay.gemm_cfg == 2
+    assert M.workspace_layout(_d(), 64, 8).tile_m == 16
