@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused mixed-precision MoE layer on one MI355X.
+
+    python bench.py [--workload dsv3_decode_mxfp4_bf16] [--steps K] [--warmup W]
+
+One step = one pass of the whole layer (routing, token quantisation, GEMM1 +
+SwiGLU, FC2 input, GEMM2, finalize) over one batch of synthetic tokens with
+inputs and packed weights already resident in HBM.  Prints ONE JSON line.
+
+The default workload is the DeepSeek-V3-shaped decode batch (64 tokens, 256
+experts, top-8, hidden 7168, intermediate 2048, MXFP4 weights x BF16
+activations), which is bound by HBM bandwidth: the roofline entry reports the
+GEMM1 kernel's achieved bytes (packed W1 codes + E8M0 scales of every expert
+that receives a token) per launch over its average launch duration, measured
+with HIP events recorded by the library on the kernel's stream.  Prefill
+workloads report GEMM1 FLOP/s against the FP8 (or BF16) MFMA peak instead.
+
+cpu_baseline: the CPU oracle (float64 NumPy), timed on this host on a bounded
+sample of tokens of the same workload, with expert weights drawn by the host
+generator and quantised before the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import moe_inputs as MI  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
+METRIC = "fused-MoE tokens/s + % MFMA peak (prefill) / % HBM GB/s (decode), 1 GPU"
+ORACLE_SAMPLE_TOKENS = {"tiny_mxfp4_fp8": 16, "dsv3_decode_mxfp4_bf16": 4,
+                        "dsv3_prefill_mxfp4_fp8": 4, "dsv4pro_prefill_mxfp4_fp8": 3,
+                        "dsv3_int4_fp8": 4}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_decode_mxfp4_bf16", choices=sorted(MI.WORKLOADS))
+    ap.add_argument("--weights", default="device", choices=["device", "host"],
+                    help="draw float32 masters on the device (torch Philox, fast) or with the "
+                         "host generator shared with the oracle (slow for 256+ experts)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def device_weights(d, wl, torch, chunk=8):
+    """Packed weights from float32 N(0, 0.02) masters drawn on the device."""
+    import mixed_precision_moe_topk_amd as M
+
+    wb, sb = M.weights_query(d)
+    weights = torch.empty(wb, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(sb, dtype=torch.uint8, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed)
+    for e0 in range(0, wl.experts, chunk):
+        n = min(chunk, wl.experts - e0)
+        w1 = torch.randn((n, 2 * wl.inter, wl.hidden), generator=g, device="cuda") * 0.02
+        w2 = torch.randn((n, wl.hidden, wl.inter), generator=g, device="cuda") * 0.02
+        M.prepare_weights(d, w1, w2, e0, weights, scales)
+        del w1, w2
+    torch.cuda.synchronize()
+    return weights, scales
+
+
+def cpu_baseline(wl):
+    import oracle as O
+
+    s = min(ORACLE_SAMPLE_TOKENS.get(wl.key, 4), wl.tokens)
+    hb = MI.hidden_bf16(wl.seed, wl.tokens, wl.hidden)[:s]
+    lg = MI.router_logits(wl.seed, wl.tokens, wl.experts, wl.bias_sigma)[:s]
+    ids, _ = O.route(lg, wl.top_k)
+    need = sorted(set(ids.reshape(-1).tolist()))
+    cache = {}
+    for e in need:  # quantised before the timed region
+        w1, w2 = MI.expert_weights(wl.seed, e, wl.hidden, wl.inter)
+        cache[e] = O.quantize_expert(w1, w2, wl.wfmt)
+    t0 = time.perf_counter()
+    O.forward(hb, lg, wl.top_k, lambda e: cache[e], wl.wfmt, wl.afmt)
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"value": round(s / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {s} tokens of the workload ({len(need)} experts), float64 oracle "
+                      f"routing->output, {dt:.2f} s; weights quantised beforehand"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        return 2
+    import torch
+
+    import mixed_precision_moe_topk_amd as M
+
+    wl = MI.WORKLOADS[args.workload]
+    d = M.LayerDims(wl.experts, wl.hidden, wl.inter, wl.wfmt, wl.afmt)
+    print(f"# workload {wl.key}: preparing weights ({args.weights})", file=sys.stderr, flush=True)
+    if args.weights == "device":
+        weights, scales = device_weights(d, wl, torch)
+    else:
+        from mixed_precision_moe_topk_amd.staging import prepare_from_host
+        weights, scales = prepare_from_host(
+            d, MI.expert_weights_many(wl.seed, range(wl.experts), wl.hidden, wl.inter))
+    hidden = torch.from_numpy(MI.hidden_bf16(wl.seed, wl.tokens, wl.hidden).view(np.int16)).cuda()
+    logits = torch.from_numpy(MI.router_logits(wl.seed, wl.tokens, wl.experts, wl.bias_sigma)).cuda()
+    out = torch.empty((wl.tokens, wl.hidden), dtype=torch.int16, device="cuda")
+    lay = M.workspace_layout(d, wl.tokens, wl.top_k)
+    ws = torch.empty(lay.total, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    print(f"# warmup {args.warmup}, timed {args.steps}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        M.run_ws(d, hidden, logits, weights, scales, wl.top_k, out, ws, stream=stream)
+    torch.cuda.synchronize()
+    M.trace_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        M.run_ws(d, hidden, logits, weights, scales, wl.top_k, out, ws, stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    M.trace_enable(False)
+    calls, stage_ms = M.trace_read()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_avg = {k: v / max(calls, 1) for k, v in stage_ms.items()}
+
+    offsets = ws[lay.offsets:lay.offsets + 4 * (wl.experts + 1)].cpu().numpy().view(np.int32)
+    active = int(np.count_nonzero(np.diff(offsets)))
+    rows = wl.tokens * wl.top_k
+    wbytes, sbytes = M.weights_query(d)
+    per_expert = (wbytes + sbytes) / wl.experts
+    # packed W1 of one expert: 2I x H E2M1/INT4 codes plus its scales
+    w1_codes = wl.inter * wl.hidden
+    if wl.wfmt == "mxfp4":
+        w1_scales = 2 * wl.inter * (-(-wl.hidden // 512)) * 16
+    else:
+        w1_scales = 2 * wl.inter * (wl.hidden // 128) * 4
+    gemm1_bytes = active * (w1_codes + w1_scales)
+    gemm1_flops = 2.0 * rows * 2 * wl.inter * wl.hidden
+    g1_s = stage_avg["gemm1"] / 1e3
+    if wl.regime in ("hbm", "latency"):
+        achieved = gemm1_bytes / g1_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = gemm1_flops / g1_s / 1e12
+        peak = MFMA_PEAK_TFLOPS[wl.afmt]
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+    roof["kernel"] = "gemm1"
+    roof["kernel_ms"] = round(stage_avg["gemm1"], 4)
+
+    layer_bytes = active * per_expert
+    layer_flops = 6.0 * rows * wl.inter * wl.hidden
+    rec = {
+        "metric": METRIC,
+        "value": round(wl.tokens / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.afmt == "bf16" else "fp8",
+        "data": "synthetic",
+        "config": {"workload": wl.key, "tokens": wl.tokens, "experts": wl.experts,
+                   "top_k": wl.top_k, "hidden": wl.hidden, "inter": wl.inter,
+                   "weights": wl.wfmt, "activations": wl.afmt, "active_experts": active,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "layer": {"weight_GBps": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),
+                  "hbm_frac": round(layer_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "gemm_TFLOPs": round(layer_flops / (ms_per_step / 1e3) / 1e12, 1),
+                  "stage_ms": {k: round(v, 4) for k, v in stage_avg.items()}},
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -28,9 +28,6 @@ magnitude rounds to zero.
 """
 from __future__ import annotations
 
-import concurrent.futures as _cf
-import os
-
 import numpy as np
 
 # ----------------------------------------------------------------------------
@@ -64,18 +61,9 @@ def _nearest_even(a: np.ndarray, grid: np.ndarray) -> np.ndarray:
     chunks (same result, less memory traffic)."""
     flat = a.reshape(-1)
     out = np.empty(flat.shape, dtype=np.int64)
-    step = 1 << 18
-
-    def work(i):
+    step = 1 << 16
+    for i in range(0, flat.size, step):
         out[i:i + step] = _nearest_even_chunk(flat[i:i + step], grid)
-
-    starts = range(0, flat.size, step)
-    if flat.size > 4 * step:
-        with _cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as pool:
-            list(pool.map(work, starts))
-    else:
-        for i in starts:
-            work(i)
     return out.reshape(a.shape)
 
 

@@ -20,9 +20,28 @@ TEST INFRASTRUCTURE ONLY: nothing on the GPU path may import this module.
 """
 from __future__ import annotations
 
+import concurrent.futures as _cf
+import os
+
 import numpy as np
 
 from . import formats as F
+
+_POOL = None
+
+
+def _rows_parallel(n_rows: int, fn, min_rows: int = 64):
+    """Runs fn(slice) over row ranges on a thread pool (rows are independent;
+    NumPy releases the GIL inside its loops).  Same result as fn(slice(0, n))."""
+    global _POOL
+    workers = min(16, os.cpu_count() or 1)
+    if n_rows < 2 * min_rows or workers == 1:
+        fn(slice(0, n_rows))
+        return
+    if _POOL is None:
+        _POOL = _cf.ThreadPoolExecutor(max_workers=workers)
+    step = max(min_rows, -(-n_rows // (4 * workers)))
+    list(_POOL.map(fn, [slice(i, min(i + step, n_rows)) for i in range(0, n_rows, step)]))
 
 MX_BLOCK = 32
 INT4_GROUP = 128
@@ -40,24 +59,36 @@ def mxfp4_quantize(w: np.ndarray):
     w = np.asarray(w, dtype=np.float32)
     n, k = w.shape
     assert k % MX_BLOCK == 0
-    blk = w.reshape(n, k // MX_BLOCK, MX_BLOCK).astype(np.float64)
-    amax = np.max(np.abs(blk), axis=-1)
-    nz = amax > 0
-    x = np.where(nz, floor_log2(np.where(nz, amax, 1.0)) - F.E2M1_EMAX, 0)
-    x = np.maximum(x, -127)
-    scale_code = (x + 127).astype(np.uint8)
-    v = np.ldexp(blk, -x[..., None])  # exact power-of-two scaling in float64
-    codes = F.e2m1_encode(v).reshape(n, k)
-    return F.pack_nibbles(codes), scale_code
+    packed = np.empty((n, k // 2), dtype=np.uint8)
+    scale_code = np.empty((n, k // MX_BLOCK), dtype=np.uint8)
+
+    def rows(sl):
+        blk = w[sl].reshape(-1, k // MX_BLOCK, MX_BLOCK).astype(np.float64)
+        amax = np.max(np.abs(blk), axis=-1)
+        nz = amax > 0
+        x = np.where(nz, floor_log2(np.where(nz, amax, 1.0)) - F.E2M1_EMAX, 0)
+        x = np.maximum(x, -127)
+        scale_code[sl] = (x + 127).astype(np.uint8)
+        v = np.ldexp(blk, -x[..., None])  # exact power-of-two scaling in float64
+        packed[sl] = F.pack_nibbles(F.e2m1_encode(v).reshape(-1, k))
+
+    _rows_parallel(n, rows)
+    return packed, scale_code
 
 
 def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """Packed MXFP4 [N, K/2] + E8M0 [N, K/32] -> float64 [N, K] (exact)."""
     n = codes.shape[0]
-    el = F.e2m1_decode(F.unpack_nibbles(codes))
-    k = el.shape[1]
-    sc = F.e8m0_decode(scales)
-    return (el.reshape(n, k // MX_BLOCK, MX_BLOCK) * sc[..., None]).reshape(n, k)
+    k = codes.shape[1] * 2
+    out = np.empty((n, k), dtype=np.float64)
+
+    def rows(sl):
+        el = F.e2m1_decode(F.unpack_nibbles(codes[sl]))
+        sc = F.e8m0_decode(scales[sl])
+        out[sl] = (el.reshape(-1, k // MX_BLOCK, MX_BLOCK) * sc[..., None]).reshape(-1, k)
+
+    _rows_parallel(n, rows)
+    return out
 
 
 def int4_quantize(w: np.ndarray):
@@ -65,29 +96,52 @@ def int4_quantize(w: np.ndarray):
     w = np.asarray(w, dtype=np.float32)
     n, k = w.shape
     assert k % INT4_GROUP == 0
-    grp = w.reshape(n, k // INT4_GROUP, INT4_GROUP)
-    amax = np.max(np.abs(grp), axis=-1)
-    s = np.where(amax > 0, amax / np.float32(7.0), np.float32(1.0)).astype(np.float32)
-    r = (grp / s[..., None]).astype(np.float32)
-    q = np.clip(np.rint(r), -8, 7).astype(np.int64).reshape(n, k)
-    return F.pack_nibbles((q & 0xF).astype(np.uint8)), s
+    packed = np.empty((n, k // 2), dtype=np.uint8)
+    s_all = np.empty((n, k // INT4_GROUP), dtype=np.float32)
+
+    def rows(sl):
+        grp = w[sl].reshape(-1, k // INT4_GROUP, INT4_GROUP)
+        amax = np.max(np.abs(grp), axis=-1)
+        s = np.where(amax > 0, amax / np.float32(7.0), np.float32(1.0)).astype(np.float32)
+        r = (grp / s[..., None]).astype(np.float32)
+        q = np.clip(np.rint(r), -8, 7).astype(np.int64).reshape(-1, k)
+        packed[sl] = F.pack_nibbles((q & 0xF).astype(np.uint8))
+        s_all[sl] = s
+
+    _rows_parallel(n, rows)
+    return packed, s_all
 
 
 def int4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     n = codes.shape[0]
-    q = F.int4_decode(F.unpack_nibbles(codes)).astype(np.float64)
-    k = q.shape[1]
-    return (q.reshape(n, k // INT4_GROUP, INT4_GROUP)
-            * scales.astype(np.float64)[..., None]).reshape(n, k)
+    k = codes.shape[1] * 2
+    out = np.empty((n, k), dtype=np.float64)
+
+    def rows(sl):
+        q = F.int4_decode(F.unpack_nibbles(codes[sl])).astype(np.float64)
+        out[sl] = (q.reshape(-1, k // INT4_GROUP, INT4_GROUP)
+                   * scales[sl].astype(np.float64)[..., None]).reshape(-1, k)
+
+    _rows_parallel(n, rows)
+    return out
 
 
 def e4m3_rows(x: np.ndarray):
     """Row-wise E4M3 quantisation: x float32 [R, C] -> (codes uint8 [R, C], s float32 [R])."""
     x = np.asarray(x, dtype=np.float32)
-    amax = np.max(np.abs(x), axis=-1)
-    s = np.where(amax > 0, amax / np.float32(F.E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    v = (x / s[:, None]).astype(np.float32)
-    return F.e4m3_encode(v), s
+    codes = np.empty(x.shape, dtype=np.uint8)
+    s_all = np.empty(x.shape[0], dtype=np.float32)
+
+    def rows(sl):
+        xs = x[sl]
+        amax = np.max(np.abs(xs), axis=-1)
+        s = np.where(amax > 0, amax / np.float32(F.E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        v = (xs / s[:, None]).astype(np.float32)
+        codes[sl] = F.e4m3_encode(v)
+        s_all[sl] = s
+
+    _rows_parallel(x.shape[0], rows)
+    return codes, s_all
 
 
 def mx_exponent_spread(scales: np.ndarray) -> int:
