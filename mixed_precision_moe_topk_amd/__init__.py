@@ -24,7 +24,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_weights_query", "moe_prepare_weights",
            "moe_unpack_weights", "moe_workspace_query", "moe_workspace_layout", "moe_run_ws",
-           "moe_run")
+           "moe_run", "moe_trace_enable", "moe_trace_read")
+STAGES = ("route", "quant", "gemm1", "requant", "gemm2", "finalize")
 
 
 class MoeError(RuntimeError):
@@ -68,6 +69,8 @@ def lib():
             "moe_workspace_layout": [DP, I64, I32, ctypes.POINTER(WsLayout)],
             "moe_run_ws": [DP, P, I64, P, P, P, I32, P, P, SZ, P],
             "moe_run": [DP, P, I64, P, P, P, I32, P, P],
+            "moe_trace_enable": [I32],
+            "moe_trace_read": [ctypes.POINTER(ctypes.c_float), I32, ctypes.POINTER(I32)],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -158,3 +161,16 @@ def run(d: LayerDims, hidden, logits, weights, scales, top_k: int, out, stream=N
     T = int(hidden.shape[0])
     _check(lib().moe_run(ctypes.byref(d.c()), _ptr(hidden), T, _ptr(logits), _ptr(weights),
                          _ptr(scales), top_k, _ptr(out), _stream(stream)))
+
+
+def trace_enable(on: bool = True):
+    _check(lib().moe_trace_enable(1 if on else 0))
+
+
+def trace_read():
+    """-> (calls, {stage: summed ms}) of the calls recorded since the last read."""
+    n = len(STAGES)
+    arr = (ctypes.c_float * n)()
+    calls = ctypes.c_int32()
+    _check(lib().moe_trace_read(arr, n, ctypes.byref(calls)))
+    return calls.value, {s: float(arr[i]) for i, s in enumerate(STAGES)}

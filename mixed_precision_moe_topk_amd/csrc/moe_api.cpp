@@ -19,6 +19,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "../../include/moe.h"
 #include "moe_common.h"
@@ -137,8 +138,8 @@ moe_status layout_of(const moe_dims* d, int64_t T, int32_t k, moe_ws_layout* L) 
     return fail(MOE_ERR_INVALID_ARG, "num_tokens %lld too large", (long long)T);
   const int64_t E = d->num_experts, H = d->hidden, I = d->inter;
   const int cfg = pick_cfg(rows, d->num_experts);
-  const int tile_m = moe::gemm_cfg(cfg).bm();
-  const int64_t nchunks = cdiv(rows, moe::kRouteChunk);
+  const int tile_m = moe::gemm_cfg(cfg, d->afmt == MOE_A_BF16).bm();
+  const int64_t nchunks = cdiv(T, moe::kRouteChunkTokens);
   const int64_t max_tiles = cdiv(rows, tile_m) + std::min<int64_t>(E, rows);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -190,9 +191,73 @@ moe_status check_device() {
   return MOE_OK;
 }
 
+// ------------------------------------------------------------------ tracing
+struct TraceCall {
+  hipEvent_t ev[MOE_NUM_STAGES + 1];
+};
+
+struct Tracer {
+  std::mutex mu;
+  bool on = false;
+  std::vector<TraceCall> pool;  // events, reused across read cycles
+  size_t used = 0;
+  static constexpr size_t kMax = 4096;
+
+  // Returns the event set of a new call, or null when tracing is off/full.
+  TraceCall* next() {
+    std::lock_guard<std::mutex> lk(mu);
+    if (!on || used >= kMax) return nullptr;
+    if (used == pool.size()) {
+      TraceCall c;
+      for (auto& e : c.ev) {
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      }
+      pool.push_back(c);
+    }
+    return &pool[used++];
+  }
+};
+
+Tracer& tracer() {
+  static Tracer t;
+  return t;
+}
+
+void trace_mark(TraceCall* tc, int i, hipStream_t st) {
+  if (tc) (void)hipEventRecord(tc->ev[i], st);
+}
+
 }  // namespace
 
 extern "C" {
+
+moe_status moe_trace_enable(int32_t on) {
+  Tracer& t = tracer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.on = on != 0;
+  return ok();
+}
+
+moe_status moe_trace_read(float* stage_ms, int32_t nstages, int32_t* calls) {
+  if (!stage_ms || !calls || nstages < 0) return fail(MOE_ERR_INVALID_ARG, "bad output arguments");
+  Tracer& t = tracer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  for (int i = 0; i < nstages; ++i) stage_ms[i] = 0.0f;
+  for (size_t c = 0; c < t.used; ++c) {
+    TraceCall& tc = t.pool[c];
+    hipError_t e = hipEventSynchronize(tc.ev[MOE_NUM_STAGES]);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+    for (int i = 0; i < nstages && i < MOE_NUM_STAGES; ++i) {
+      float ms = 0.0f;
+      e = hipEventElapsedTime(&ms, tc.ev[i], tc.ev[i + 1]);
+      if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
+      stage_ms[i] += ms;
+    }
+  }
+  *calls = (int32_t)t.used;
+  t.used = 0;
+  return ok();
+}
 
 int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
 
@@ -301,6 +366,8 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
     return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes,
                 L.total);
   MOE_TRY(check_device());
+  TraceCall* tc = tracer().next();
+  trace_mark(tc, 0, stream);
 
   const Sizes s = sizes_of(dims);
   const int64_t T = num_tokens, rows = T * top_k;
@@ -316,7 +383,7 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
   rp.ids = reinterpret_cast<int32_t*>(ws + L.ids);
   rp.weights = reinterpret_cast<float*>(ws + L.topk_w);
   rp.chunk_counts = reinterpret_cast<int32_t*>(ws + L.chunk_counts);
-  rp.nchunks = (int32_t)cdiv(rows, moe::kRouteChunk);
+  rp.nchunks = (int32_t)cdiv(T, moe::kRouteChunkTokens);
   rp.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
   rp.row_token = reinterpret_cast<int32_t*>(ws + L.row_token);
   rp.slot_row = reinterpret_cast<int32_t*>(ws + L.slot_row);
@@ -324,6 +391,7 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
   rp.num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
   rp.tile_m = L.tile_m;
   MOE_TRY(hip_check(moe::launch_route(rp, stream), "route", stream));
+  trace_mark(tc, 1, stream);
 
   const float* tok_scales = nullptr;
   const uint8_t* a1 = static_cast<const uint8_t*>(hidden);
@@ -337,9 +405,10 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
     a1 = codes;
     a1_stride = H;
   }
+  trace_mark(tc, 2, stream);
 
   const int variant = variant_of(dims);
-  const moe::GemmCfg cfg = moe::gemm_cfg(L.gemm_cfg);
+  const moe::GemmCfg cfg = moe::gemm_cfg(L.gemm_cfg, !fp8);
   const uint8_t* wbytes = static_cast<const uint8_t*>(weights);
   const uint8_t* sbytes = static_cast<const uint8_t*>(scales);
   float* h = reinterpret_cast<float*>(ws + L.h);
@@ -357,16 +426,18 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
   g1.num_tiles = rp.num_tiles;
   g1.K = H;
   g1.N = 2 * I;
-  g1.n_tiles = (2 * I) / cfg.bn();
+  g1.n_tiles = (int32_t)cdiv(2 * I, cfg.bn());
   g1.out = h;
   g1.out_stride = I;
   MOE_TRY(hip_check(moe::launch_gemm(variant, true, L.gemm_cfg, g1, L.max_tiles, stream),
                     "gemm1", stream));
+  trace_mark(tc, 3, stream);
 
   uint8_t* q2 = ws + L.fc2_codes;
   float* s2 = reinterpret_cast<float*>(ws + L.fc2_scales);
   MOE_TRY(hip_check(moe::launch_requant(h, rows, I, fp8 ? 0 : 1, q2, s2, stream),
                     "fc2 requant", stream));
+  trace_mark(tc, 4, stream);
 
   float* y2 = reinterpret_cast<float*>(ws + L.y2);
   moe::GemmParams g2;
@@ -382,15 +453,17 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
   g2.num_tiles = rp.num_tiles;
   g2.K = I;
   g2.N = H;
-  g2.n_tiles = H / cfg.bn();
+  g2.n_tiles = (int32_t)cdiv(H, cfg.bn());
   g2.out = y2;
   g2.out_stride = H;
   MOE_TRY(hip_check(moe::launch_gemm(variant, false, L.gemm_cfg, g2, L.max_tiles, stream),
                     "gemm2", stream));
+  trace_mark(tc, 5, stream);
 
   MOE_TRY(hip_check(moe::launch_finalize(y2, rp.weights, rp.slot_row, T, top_k, H,
                                          static_cast<uint16_t*>(out), stream),
                     "finalize", stream));
+  trace_mark(tc, 6, stream);
   return ok();
 }
 

@@ -12,7 +12,7 @@ constexpr int kWave = 64;
 constexpr int kKStep = 128;        // K consumed by one 16x16x128 MFMA
 constexpr int kMxBlock = 32;       // elements per E8M0 scale (OCP MX block)
 constexpr int kInt4Group = 128;    // elements per INT4 group scale
-constexpr int kRouteChunk = 1024;  // (token, slot) pairs per routing chunk
+constexpr int kRouteChunkTokens = 64;  // tokens per routing chunk (one wave)
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 1024;
 
@@ -35,6 +35,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v2s __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- numerics
 // Round a finite float to the nearest OCP E4M3 ("FN") code: ties to even
@@ -97,7 +98,7 @@ struct RouteParams {
   int32_t* ids;            // [T, k]
   float* weights;          // [T, k]
   int32_t* chunk_counts;   // [nchunks, E]
-  int32_t nchunks;
+  int32_t nchunks;         // ceil(T / kRouteChunkTokens)
   int32_t* offsets;        // [E + 1]
   int32_t* row_token;      // [T*k]
   int32_t* slot_row;       // [T*k]
@@ -143,18 +144,20 @@ hipError_t launch_unpack(int wfmt_int4, const uint8_t* codes, int64_t codes_stri
                          int32_t N, int32_t K, bool interleave_gate_up, uint8_t* out_codes,
                          uint8_t* out_scales, hipStream_t st);
 
-// GEMM tile configurations (rows per block tile; columns per block tile).
+// GEMM tile configurations (rows x device columns per block tile), chosen by
+// the mean rows per expert.  BF16 activations keep the register-direct kernel;
+// E4M3 activations use the LDS-staged kernel for the two larger shapes.
 struct GemmCfg {
   int waves_m, wm, wn;
   int bm() const { return 16 * waves_m * wm; }
   int bn() const { return 16 * (4 / waves_m) * wn; }
 };
 constexpr int kNumGemmCfg = 3;
-inline GemmCfg gemm_cfg(int i) {
+inline GemmCfg gemm_cfg(int i, bool bf16) {
   switch (i) {
-    case 0: return GemmCfg{1, 1, 2};  // 16 x 128: decode-sized experts
-    case 1: return GemmCfg{1, 3, 2};  // 48 x 128
-    default: return GemmCfg{2, 4, 4}; // 128 x 128: prefill
+    case 0: return GemmCfg{1, 1, 2};                                  // 16 x 128
+    case 1: return bf16 ? GemmCfg{1, 3, 2} : GemmCfg{1, 4, 4};        // 48 x 128 / 64 x 256
+    default: return GemmCfg{2, 4, 4};                                 // 128 x 128
   }
 }
 

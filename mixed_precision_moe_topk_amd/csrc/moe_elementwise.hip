@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ y2,
                                                   uint16_t* __restrict__ out) {
   const int64_t t = blockIdx.x;
   const int nv = H / 4;
-  for (int i = threadIdx.x; i < nv; i += blockDim.x) {
+  for (int i = blockIdx.y * blockDim.x + threadIdx.x; i < nv; i += gridDim.y * blockDim.x) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
       const float w = weights[t * k + j];
@@ -141,7 +141,9 @@ hipError_t launch_requant(const float* h, int64_t rows, int32_t I, int afmt_bf16
 hipError_t launch_finalize(const float* y2, const float* weights, const int32_t* slot_row,
                            int64_t T, int32_t k, int32_t H, uint16_t* out, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  k_finalize<<<(unsigned)T, 256, 0, st>>>(y2, weights, slot_row, k, H, out);
+  // one block per (token, 1024 columns)
+  dim3 grid((unsigned)T, (unsigned)((H / 4 + 255) / 256));
+  k_finalize<<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out);
   return hipGetLastError();
 }
 

@@ -25,6 +25,8 @@
 // Block = 4 waves (WAVES_M x WAVES_N); each wave owns WM x WN 16x16 output
 // tiles.  FC1 writes h = silu(gate) * up (gate/up rows interleaved per 16-row
 // block by the weight layout); FC2 writes y2 = acc * row scale.
+#include <type_traits>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -93,6 +95,59 @@ __device__ __forceinline__ v8bf fp4x8_to_bf16(uint32_t w, float scale) {
   return r;
 }
 
+// Epilogue shared by the GEMM kernels.  Output tile (i, j) of a wave holds, in
+// lane l, column 16*(nb0+j) + l%16 of rows row_base + 16*i + 4*(l/16) + [0, 4).
+//   FC1: tiles (2q, 2q+1) are the gate and up halves of intermediate block
+//        (nb0 + 2q)/2; h = silu(g*s) * (u*s), s = token scale.
+//   FC2: y2 = acc * s, s = row scale.
+template <bool FC1, int WM, int WN>
+__device__ __forceinline__ void epilogue(const GemmParams& p, const v4f (&acc)[WM][WN],
+                                         int row_base, int row_end, int nvalid, int64_t nb0,
+                                         int jvalid, int lane) {
+  const int col_lane = lane & 15;
+  const int row_lane = 4 * (lane >> 4);
+  if (FC1) {
+#pragma unroll
+    for (int q = 0; q < WN / 2; ++q) {
+      if (2 * q >= jvalid) continue;
+      const int64_t ib = (nb0 + 2 * q) >> 1;  // intermediate 16-column block
+      const int64_t c = ib * 16 + col_lane;
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        if (i >= nvalid) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = row_base + 16 * i + row_lane + v;
+          if (r < row_end) {
+            const float s = p.row_scale ? p.row_scale[p.row_token[r]] : 1.0f;
+            const float g = acc[i][2 * q][v] * s;
+            const float u = acc[i][2 * q + 1][v] * s;
+            p.out[(int64_t)r * p.out_stride + c] = g / (1.0f + expf(-g)) * u;
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      if (j >= jvalid) continue;
+      const int64_t c = (nb0 + j) * 16 + col_lane;
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        if (i >= nvalid) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = row_base + 16 * i + row_lane + v;
+          if (r < row_end) {
+            const float s = p.row_scale ? p.row_scale[r] : 1.0f;
+            p.out[(int64_t)r * p.out_stride + c] = acc[i][j][v] * s;
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int V, bool FC1, int WAVES_M, int WM, int WN>
 __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   constexpr int WAVES_N = 4 / WAVES_M;
@@ -116,6 +171,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   const uint8_t* wbase = p.w + e * p.w_expert_stride;
   const uint8_t* sbase = p.s + e * p.s_expert_stride;
   const int64_t nb0 = (int64_t)nt * (WAVES_N * WN) + wn * WN;
+  const int jvalid = (int)min<int64_t>(WN, p.N / 16 - nb0);  // N tail: 16-column blocks left
+  if (jvalid <= 0) return;
 
   // A row pointers (rows past the tile end re-read its last row; their
   // outputs are never stored)
@@ -160,6 +217,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     }
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
+      if (j >= jvalid) continue;
       const int64_t nb = nb0 + j;
       b[j] = *reinterpret_cast<const uint4*>(wbase + ((nb * KS + ks) * 64 + lane) * 16);
       if (V == kInt4Fp8)
@@ -181,6 +239,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
           const v8i aop = as_v8i(a[i][0], a[i][1]);
 #pragma unroll
           for (int j = 0; j < WN; ++j) {
+            if (j >= jvalid) continue;
             switch (ks & 3) {
               case 0: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, 127, 0, (int)sc[j]); break;
               case 1: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, 127, 1, (int)sc[j]); break;
@@ -200,6 +259,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
           const v8i aop = as_v8i(a[i][0], a[i][1]);
 #pragma unroll
           for (int j = 0; j < WN; ++j) {
+            if (j >= jvalid) continue;
             const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 aop, bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
             const float gs = __uint_as_float(sc[j]);
@@ -211,6 +271,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     } else {
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
+        if (j >= jvalid) continue;
         const float scale = e8m0_to_float((sc[j] >> (8 * (ks & 3))) & 0xFFu);
         const uint32_t bw[4] = {b[j].x, b[j].y, b[j].z, b[j].w};
 #pragma unroll
@@ -237,47 +298,164 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     }
   }
 
-  // epilogue
-  const int col_lane = lane & 15;
-  const int row_lane = 4 * (lane >> 4);
-  if (FC1) {
+  epilogue<FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+}
+
+
+// ----------------------------------------------------------------------------
+// LDS-staged grouped GEMM for E4M3 activations (MXFP4 x FP8, INT4 x FP8).
+// Block = 4 waves, WAVES_M x WAVES_N; each wave owns 16*WM rows and 16*WN
+// device columns.  Per 128-wide K step the block stages the tile's A rows
+// (gathered token rows for FC1) into LDS in MFMA fragment order (fragment
+// (i, h) is 1 KB, lane-major: every lane's 16-byte read is conflict-free);
+// two LDS buffers, one barrier per step.  Global loads run two steps ahead:
+// A into two register staging sets, weights (pre-shuffled, straight into the
+// MFMA operand registers) into four register sets, so a load has two steps of
+// MFMA work to arrive.  Rows past the tile end are loaded as copies of its
+// last row and never stored; 16-row subtiles past the end are skipped.
+template <int V, bool FC1, int WAVES_M, int WM, int WN>
+__global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
+  static_assert(V == kMxfp4Fp8 || V == kInt4Fp8, "E4M3 activations only");
+  static_assert(!FC1 || WN % 2 == 0, "FC1 pairs gate/up tiles");
+  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int BM = 16 * WM * WAVES_M;
+  static_assert(BM % 32 == 0, "BM must be a multiple of 32");
+  constexpr int ABUF = BM * kKStep;        // bytes of one A stage
+  constexpr int NCH = BM * 8 / 256;        // 16-byte chunks per thread per stage
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * ABUF];
+
+  const int64_t item = blockIdx.x;
+  const int64_t mt = item / p.n_tiles;
+  const int nt = (int)(item - mt * p.n_tiles);
+  if (mt >= *p.num_tiles) return;
+  const Tile tile = p.tiles[mt];
+  // wave-uniform values are made scalar so that branches on them are scalar
+  // branches (exec-masked branches make the compiler drain every outstanding
+  // load at each join, which would serialise the prefetch)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = lane_id();
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int row_end = tile.row0 + tile.nrows;
+  const int row_base = tile.row0 + 16 * WM * wm;
+  const int nvalid = __builtin_amdgcn_readfirstlane(max(0, min(WM, (row_end - row_base + 15) / 16)));
+
+  const int K = p.K;
+  const int KS = K / kKStep, KS4 = (KS + 3) / 4;
+  const int64_t e = tile.expert;
+  const uint8_t* wbase = p.w + e * p.w_expert_stride;
+  const uint8_t* sbase = p.s + e * p.s_expert_stride;
+  const int64_t nb0 = (int64_t)nt * (WAVES_N * WN) + wn * WN;
+  // N is a multiple of 128 and 16*WN divides 128, so a wave's columns are all
+  // inside N or all past it (a wave with no rows or columns still stages A
+  // and joins every barrier)
+  static_assert(128 % (16 * WN) == 0, "wave columns must tile 128");
+  const bool cols = __builtin_amdgcn_readfirstlane((int)(nb0 * 16 < p.N)) != 0;
+  const int jvalid = cols ? WN : 0;
+
+  // this thread's A chunks: tile row r, 16-byte column chunk c; source pointer
+  // and LDS destination (fragment (r/16, h), lane (r%16) + 16*g)
+  const uint8_t* asrc[NCH];
+  int adst[NCH];
 #pragma unroll
-    for (int q = 0; q < WN / 2; ++q) {
-      const int64_t ib = (nb0 + 2 * q) >> 1;  // intermediate 16-column block
-      const int64_t c = ib * 16 + col_lane;
+  for (int u = 0; u < NCH; ++u) {
+    const int q = threadIdx.x + 256 * u;
+    const int r = q >> 3, c = q & 7;
+    const int rr = min(tile.row0 + r, row_end - 1);
+    const int64_t src = FC1 ? (int64_t)p.row_token[rr] : (int64_t)rr;
+    asrc[u] = p.a + src * p.a_stride + 16 * c;
+    int g, h;
+    if (V == kMxfp4Fp8) { g = c & 3; h = c >> 2; }   // k = 64h + 16g + [0,16)
+    else { g = c >> 1; h = c & 1; }                  // k = 32g + 16h + [0,16)
+    adst[u] = ((r >> 4) * 2 + h) * 1024 + ((r & 15) + 16 * g) * 16;
+  }
+
+  v4f acc[WM][WN];
 #pragma unroll
-      for (int i = 0; i < WM; ++i) {
-        if (i >= nvalid) continue;
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = row_base + 16 * i + row_lane + v;
-          if (r < row_end) {
-            const float s = p.row_scale ? p.row_scale[p.row_token[r]] : 1.0f;
-            const float g = acc[i][2 * q][v] * s;
-            const float u = acc[i][2 * q + 1][v] * s;
-            p.out[(int64_t)r * p.out_stride + c] = g / (1.0f + expf(-g)) * u;
-          }
-        }
-      }
-    }
-  } else {
+    for (int j = 0; j < WN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  v4u ast[2][NCH];
+  uint4 bq[4][WN];
+  uint32_t sq[4][WN];
+
+  auto load_a = [&](int ks, v4u (&dst)[NCH]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) dst[u] = *reinterpret_cast<const v4u*>(asrc[u] + ks * kKStep);
+  };
+  auto store_a = [&](int buf, const v4u (&src)[NCH]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) *reinterpret_cast<v4u*>(lds + buf * ABUF + adst[u]) = src[u];
+  };
+  auto load_b = [&](int ks, uint4 (&b)[WN], uint32_t (&sc)[WN]) __attribute__((always_inline)) {
+    if (!cols) return;
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      const int64_t c = (nb0 + j) * 16 + col_lane;
+      const int64_t nb = nb0 + j;
+      b[j] = *reinterpret_cast<const uint4*>(wbase + ((nb * KS + ks) * 64 + lane) * 16);
+      if (V == kInt4Fp8)
+        sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS + ks) * 16 + (lane & 15)) * 4);
+      else
+        sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS4 + (ks >> 2)) * 64 + lane) * 4);
+    }
+  };
+
+  // K step ks with S = ks % 4 (E8M0 byte select and register-set index).
+  // Prefetch loads are unconditional (their step index is clamped to the
+  // last step) so that the steady-state loop has no branches around memory
+  // operations and the compiler's wait counts stay exact.
+  auto step = [&](auto s_c, int ks) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_c)::value;
+    const int kp = min(ks + 2, KS - 1);
+    load_a(kp, ast[S & 1]);
+    load_b(kp, bq[(S + 2) & 3], sq[(S + 2) & 3]);
+    const uint8_t* abuf = lds + (S & 1) * ABUF + (WM * wm) * 2048 + lane * 16;
+    v8i bop[WN];
 #pragma unroll
-      for (int i = 0; i < WM; ++i) {
-        if (i >= nvalid) continue;
+    for (int j = 0; j < WN; ++j)
+      bop[j] = (V == kMxfp4Fp8) ? fp4_operand(bq[S][j]) : int4_operand(bq[S][j]);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = row_base + 16 * i + row_lane + v;
-          if (r < row_end) {
-            const float s = p.row_scale ? p.row_scale[r] : 1.0f;
-            p.out[(int64_t)r * p.out_stride + c] = acc[i][j][v] * s;
+    for (int i = 0; i < WM; ++i) {
+      if (cols && i < nvalid) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(abuf + (2 * i) * 1024);
+        const uint4 hi = *reinterpret_cast<const uint4*>(abuf + (2 * i + 1) * 1024);
+        const v8i aop = as_v8i(lo, hi);
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          if (V == kMxfp4Fp8) {
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                aop, bop[j], acc[i][j], 0, 4, 0, 127, S, (int)sq[S][j]);
+          } else {
+            const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                aop, bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+            const float gs = __uint_as_float(sq[S][j]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[i][j][v] += part[v] * gs;
           }
         }
       }
     }
+    // A of step ks+1 (a harmless copy of the last step once past the end)
+    store_a((S + 1) & 1, ast[(S + 1) & 1]);
+    __syncthreads();
+  };
+
+  load_a(0, ast[0]);
+  load_b(0, bq[0], sq[0]);
+  load_a(min(1, KS - 1), ast[1]);
+  load_b(min(1, KS - 1), bq[1], sq[1]);
+  store_a(0, ast[0]);
+  __syncthreads();
+  int ks = 0;
+  for (; ks + 4 <= KS; ks += 4) {
+    step(std::integral_constant<int, 0>{}, ks);
+    step(std::integral_constant<int, 1>{}, ks + 1);
+    step(std::integral_constant<int, 2>{}, ks + 2);
+    step(std::integral_constant<int, 3>{}, ks + 3);
   }
+  if (ks < KS) step(std::integral_constant<int, 0>{}, ks);
+  if (ks + 1 < KS) step(std::integral_constant<int, 1>{}, ks + 1);
+  if (ks + 2 < KS) step(std::integral_constant<int, 2>{}, ks + 2);
+  epilogue<FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
 template <int V, bool FC1>
@@ -287,8 +465,14 @@ static hipError_t launch_v(int cfg, const GemmParams& p, int64_t max_tiles, hipS
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   switch (cfg) {
     case 0: k_gemm<V, FC1, 1, 1, 2><<<(unsigned)blocks, 256, 0, st>>>(p); break;
-    case 1: k_gemm<V, FC1, 1, 3, 2><<<(unsigned)blocks, 256, 0, st>>>(p); break;
-    default: k_gemm<V, FC1, 2, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p); break;
+    case 1:
+      if constexpr (V == kMxfp4Bf16) k_gemm<V, FC1, 1, 3, 2><<<(unsigned)blocks, 256, 0, st>>>(p);
+      else k_gemm_lds<V, FC1, 1, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p);
+      break;
+    default:
+      if constexpr (V == kMxfp4Bf16) k_gemm<V, FC1, 2, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p);
+      else k_gemm_lds<V, FC1, 2, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p);
+      break;
   }
   return hipGetLastError();
 }

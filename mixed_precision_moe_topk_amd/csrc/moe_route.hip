@@ -89,101 +89,102 @@ __global__ __launch_bounds__(256) void k_router(RouteParams p) {
   }
 }
 
-// Per chunk of kRouteChunk (token, slot) pairs: expert histogram.
-__global__ __launch_bounds__(256) void k_route_count(RouteParams p) {
-  __shared__ int32_t cnt[kMaxExperts];
-  const int64_t total = p.tokens * p.top_k;
-  const int64_t base = (int64_t)blockIdx.x * kRouteChunk;
-  for (int e = threadIdx.x; e < p.experts; e += blockDim.x) cnt[e] = 0;
+// Routing index over chunks of kChunkTokens tokens (one wave per chunk).  For
+// every expert a 64-bit mask of the chunk's tokens that selected it is built
+// with atomic ORs in LDS (order-independent, so deterministic); the rank of
+// token t among the chunk's rows of expert e is popcount(mask[e] & lanes < t).
+// Rows of one expert thus come in ascending (token, slot) order.
+constexpr int kChunkTokens = kRouteChunkTokens;
+
+__device__ __forceinline__ void build_masks(const RouteParams& p, uint64_t* mask, int64_t t0) {
+  const int lane = lane_id();
+  for (int e = lane; e < p.experts; e += kWave) mask[e] = 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < kRouteChunk; i += blockDim.x) {
-    const int64_t f = base + i;
-    if (f < total) atomicAdd(&cnt[p.ids[f]], 1);
+  const int64_t t = t0 + lane;
+  if (t < p.tokens) {
+    for (int j = 0; j < p.top_k; ++j)
+      atomicOr(reinterpret_cast<unsigned long long*>(&mask[p.ids[t * p.top_k + j]]),
+               1ull << lane);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < p.experts; e += blockDim.x)
-    p.chunk_counts[(int64_t)blockIdx.x * p.experts + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(64) void k_route_count(RouteParams p) {
+  __shared__ uint64_t mask[kMaxExperts];
+  build_masks(p, mask, (int64_t)blockIdx.x * kChunkTokens);
+  for (int e = lane_id(); e < p.experts; e += kWave)
+    p.chunk_counts[(int64_t)blockIdx.x * p.experts + e] = __popcll(mask[e]);
 }
 
 // Single block: per-expert totals, chunk bases, expert offsets, tile list.
 __global__ __launch_bounds__(1024) void k_route_scan(RouteParams p) {
   __shared__ int32_t tot[kMaxExperts];
   __shared__ int32_t ntl[kMaxExperts];
+  __shared__ int32_t wsum[2][16];
   const int E = p.experts;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int32_t run = 0;
+  const int e = threadIdx.x;  // blockDim.x == 1024 >= E
+  int32_t run = 0;
+  if (e < E) {
     for (int c = 0; c < p.nchunks; ++c) {
       const int64_t idx = (int64_t)c * E + e;
       const int32_t v = p.chunk_counts[idx];
       p.chunk_counts[idx] = run;  // rows of this expert in earlier chunks
       run += v;
     }
-    tot[e] = run;
-    ntl[e] = (run + p.tile_m - 1) / p.tile_m;
+  }
+  const int32_t nt = (run + p.tile_m - 1) / p.tile_m;
+  // block-wide exclusive scans of run and nt (wave scans + wave totals)
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  int32_t a = run, b = nt;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t ya = __shfl_up(a, o), yb = __shfl_up(b, o);
+    if (lane >= o) { a += ya; b += yb; }
+  }
+  if (lane == kWave - 1) { wsum[0][w] = a; wsum[1][w] = b; }
+  __syncthreads();
+  int32_t pa = 0, pb = 0;
+  for (int i = 0; i < w; ++i) { pa += wsum[0][i]; pb += wsum[1][i]; }
+  const int32_t ex_a = pa + a - run, ex_b = pb + b - nt;
+  if (e < E) {
+    p.offsets[e] = ex_a;
+    tot[e] = ex_a;
+    ntl[e] = ex_b;
+  }
+  if (e == E - 1) {
+    p.offsets[E] = ex_a + run;
+    *p.num_tiles = ex_b + nt;
   }
   __syncthreads();
-  // exclusive scans over experts (E <= 1024: one thread does the short serial
-  // scan; it is a few hundred adds)
-  if (threadIdx.x == 0) {
-    int32_t r = 0, tl = 0;
-    for (int e = 0; e < E; ++e) {
-      const int32_t c = tot[e], n = ntl[e];
-      p.offsets[e] = r;
-      tot[e] = r;
-      ntl[e] = tl;
-      r += c;
-      tl += n;
-    }
-    p.offsets[E] = r;
-    *p.num_tiles = tl;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+  if (e < E) {
     const int32_t start = tot[e];
-    const int32_t cnt = p.offsets[e + 1] - start;
     int32_t ti = ntl[e];
-    for (int32_t r = 0; r < cnt; r += p.tile_m, ++ti) {
+    for (int32_t r = 0; r < run; r += p.tile_m, ++ti) {
       Tile tl;
       tl.expert = e;
       tl.row0 = start + r;
-      tl.nrows = min(p.tile_m, cnt - r);
+      tl.nrows = min(p.tile_m, run - r);
       tl.pad = 0;
       p.tiles[ti] = tl;
     }
   }
 }
 
-// One wave per chunk: stable placement of each (token, slot) pair into its
-// expert's rows in ascending (token, slot) order.
 __global__ __launch_bounds__(64) void k_route_scatter(RouteParams p) {
-  __shared__ int32_t cursor[kMaxExperts];
+  __shared__ uint64_t mask[kMaxExperts];
+  const int64_t t0 = (int64_t)blockIdx.x * kChunkTokens;
+  build_masks(p, mask, t0);
   const int lane = lane_id();
-  const int64_t total = p.tokens * p.top_k;
-  const int64_t base = (int64_t)blockIdx.x * kRouteChunk;
-  for (int e = lane; e < p.experts; e += kWave)
-    cursor[e] = p.offsets[e] + p.chunk_counts[(int64_t)blockIdx.x * p.experts + e];
-  __syncthreads();
-  for (int it = 0; it < kRouteChunk; it += kWave) {
-    const int64_t f = base + it + lane;
-    const bool valid = f < total;
-    const int e = valid ? p.ids[f] : -1;
-    uint64_t rem = __ballot(valid);
-    int pos = 0;
-    while (rem) {
-      const int leader = __ffsll((unsigned long long)rem) - 1;
-      const int el = __shfl(e, leader);
-      const bool mine = valid && e == el;
-      const uint64_t m = __ballot(mine) & rem;
-      if (mine) pos = cursor[el] + __popcll(m & ((1ull << lane) - 1ull));
-      __builtin_amdgcn_wave_barrier();
-      if (lane == leader) cursor[el] += __popcll(m);
-      __builtin_amdgcn_wave_barrier();
-      rem &= ~m;
-    }
-    if (valid) {
-      p.row_token[pos] = (int32_t)(f / p.top_k);
-      p.slot_row[f] = pos;
-    }
+  const int64_t t = t0 + lane;
+  if (t >= p.tokens) return;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int j = 0; j < p.top_k; ++j) {
+    const int64_t f = t * p.top_k + j;
+    const int e = p.ids[f];
+    const int pos = p.offsets[e] + p.chunk_counts[(int64_t)blockIdx.x * p.experts + e] +
+                    __popcll(mask[e] & below);
+    p.row_token[pos] = (int32_t)t;
+    p.slot_row[f] = pos;
   }
 }
 
@@ -191,7 +192,7 @@ hipError_t launch_route(const RouteParams& p, hipStream_t st) {
   if (p.tokens == 0) return hipSuccess;
   const int wpb = 4;
   k_router<<<(unsigned)((p.tokens + wpb - 1) / wpb), wpb * kWave, 0, st>>>(p);
-  k_route_count<<<p.nchunks, 256, 0, st>>>(p);
+  k_route_count<<<p.nchunks, 64, 0, st>>>(p);
   k_route_scan<<<1, 1024, 0, st>>>(p);
   k_route_scatter<<<p.nchunks, 64, 0, st>>>(p);
   return hipGetLastError();
