@@ -22,13 +22,34 @@ enum Variant : int {
   kInt4Fp8 = 2,    // INT4 weights (fp32 / 128) x per-token E4M3 activations
 };
 
-// Work item of the grouped GEMMs: rows [row0, row0 + nrows) of expert `expert`.
+// Work-map entry of the grouped GEMMs: rows [row0, row0 + nrows) of expert
+// `expert` (entries are grouped by expert, in expert order).
 struct Tile {
   int32_t expert;
   int32_t row0;
   int32_t nrows;
   int32_t pad;
 };
+
+// Block -> (tile, N-tile) map shared by the GEMM kernels.  The hardware hands
+// consecutive workgroups to the 8 XCDs in turn, so block b runs on XCD b % 8;
+// each XCD gets a contiguous range of work items (item = tile * n_tiles +
+// N-tile), so all N-tiles of an M-tile run together on one XCD and its
+// activation rows are fetched into that XCD's L2 once.  The grid is a
+// multiple of 8 and covers every item once; blocks past the end return false.
+__device__ __forceinline__ bool work_item(const Tile* tiles, const int32_t* num_tiles,
+                                          int32_t n_tiles, Tile* tile, int* nt) {
+  const int64_t total = (int64_t)(*num_tiles) * n_tiles;
+  const int64_t per = (total + 7) / 8;
+  const int64_t b = blockIdx.x;
+  if (b / 8 >= per) return false;
+  const int64_t item = (b % 8) * per + b / 8;
+  if (item >= total) return false;
+  const int64_t mt = item / n_tiles;
+  *nt = (int)(item - mt * n_tiles);
+  *tile = tiles[mt];
+  return true;
+}
 
 // ---------------------------------------------------------------- vectors
 typedef int v8i __attribute__((ext_vector_type(8)));

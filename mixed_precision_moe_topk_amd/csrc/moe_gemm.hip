@@ -153,11 +153,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int NA = Frag<V>::kA;
   static_assert(!FC1 || WN % 2 == 0, "FC1 pairs gate/up tiles");
-  const int64_t item = blockIdx.x;
-  const int64_t mt = item / p.n_tiles;
-  const int nt = (int)(item - mt * p.n_tiles);
-  if (mt >= *p.num_tiles) return;
-  const Tile tile = p.tiles[mt];
+  Tile tile;
+  int nt;
+  if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int row_base = tile.row0 + 16 * WM * wm;
@@ -306,9 +304,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
 // LDS-staged grouped GEMM for E4M3 activations (MXFP4 x FP8, INT4 x FP8).
 // Block = 4 waves, WAVES_M x WAVES_N; each wave owns 16*WM rows and 16*WN
 // device columns.  Per 128-wide K step the block stages the tile's A rows
-// (gathered token rows for FC1) into LDS in MFMA fragment order (fragment
-// (i, h) is 1 KB, lane-major: every lane's 16-byte read is conflict-free);
-// two LDS buffers, one barrier per step.  Global loads run two steps ahead:
+// (gathered token rows for FC1) into LDS in MFMA fragment order: fragment
+// (i, h) is 1 KB holding the 16-byte operand pieces of its 64 lanes; lane
+// L = rho + 16g sits in 16-byte slot 16g + (rho ^ ((2g + h) | (rho & 1) << 3)),
+// an XOR swizzle that keeps both the staging writes (8 threads = one row's 8
+// chunks, 16 threads = two rows) and the fragment reads (consecutive lanes)
+// on distinct LDS banks at 8- and 16-lane granularity.  Two LDS buffers, one
+// barrier per step.  Global loads run two steps ahead:
 // A into two register staging sets, weights (pre-shuffled, straight into the
 // MFMA operand registers) into four register sets, so a load has two steps of
 // MFMA work to arrive.  Rows past the tile end are loaded as copies of its
@@ -324,11 +326,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
   constexpr int NCH = BM * 8 / 256;        // 16-byte chunks per thread per stage
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * ABUF];
 
-  const int64_t item = blockIdx.x;
-  const int64_t mt = item / p.n_tiles;
-  const int nt = (int)(item - mt * p.n_tiles);
-  if (mt >= *p.num_tiles) return;
-  const Tile tile = p.tiles[mt];
+  Tile tile;
+  int nt;
+  if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
   // wave-uniform values are made scalar so that branches on them are scalar
   // branches (exec-masked branches make the compiler drain every outstanding
   // load at each join, which would serialise the prefetch)
@@ -365,8 +365,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
     int g, h;
     if (V == kMxfp4Fp8) { g = c & 3; h = c >> 2; }   // k = 64h + 16g + [0,16)
     else { g = c >> 1; h = c & 1; }                  // k = 32g + 16h + [0,16)
-    adst[u] = ((r >> 4) * 2 + h) * 1024 + ((r & 15) + 16 * g) * 16;
+    const int rho = r & 15;
+    adst[u] = ((r >> 4) * 2 + h) * 1024 + (16 * g + (rho ^ ((2 * g + h) | ((rho & 1) << 3)))) * 16;
   }
+  // this lane's read offsets inside a fragment of half h = 0 / 1
+  const int rho_l = lane & 15, g_l = lane >> 4;
+  const int rd0 = (16 * g_l + (rho_l ^ ((2 * g_l) | ((rho_l & 1) << 3)))) * 16;
+  const int rd1 = 1024 + (16 * g_l + (rho_l ^ ((2 * g_l + 1) | ((rho_l & 1) << 3)))) * 16;
 
   v4f acc[WM][WN];
 #pragma unroll
@@ -408,7 +413,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
     const int kp = min(ks + 2, KS - 1);
     load_a(kp, ast[S & 1]);
     load_b(kp, bq[(S + 2) & 3], sq[(S + 2) & 3]);
-    const uint8_t* abuf = lds + (S & 1) * ABUF + (WM * wm) * 2048 + lane * 16;
+    const uint8_t* abuf = lds + (S & 1) * ABUF + (WM * wm) * 2048;
     v8i bop[WN];
 #pragma unroll
     for (int j = 0; j < WN; ++j)
@@ -416,8 +421,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       if (cols && i < nvalid) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(abuf + (2 * i) * 1024);
-        const uint4 hi = *reinterpret_cast<const uint4*>(abuf + (2 * i + 1) * 1024);
+        const uint4 lo = *reinterpret_cast<const uint4*>(abuf + (2 * i) * 1024 + rd0);
+        const uint4 hi = *reinterpret_cast<const uint4*>(abuf + (2 * i) * 1024 + rd1);
         const v8i aop = as_v8i(lo, hi);
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
 
 template <int V, bool FC1>
 static hipError_t launch_v(int cfg, const GemmParams& p, int64_t max_tiles, hipStream_t st) {
-  const int64_t blocks = max_tiles * p.n_tiles;
+  const int64_t blocks = (max_tiles * p.n_tiles + 7) / 8 * 8;  // work_item needs a multiple of 8
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   switch (cfg) {
