@@ -36,6 +36,7 @@ import moe_inputs as MI  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
+COPY_CALIB_BYTES = 256 << 20
 METRIC = "fused-MoE tokens/s + % MFMA peak (prefill) / % HBM GB/s (decode), 1 GPU"
 ORACLE_SAMPLE_TOKENS = {"tiny_mxfp4_fp8": 16, "dsv3_decode_mxfp4_bf16": 4,
                         "dsv3_prefill_mxfp4_fp8": 4, "dsv4pro_prefill_mxfp4_fp8": 3,
@@ -119,6 +120,14 @@ def main():
     lay = M.workspace_layout(d, wl.tokens, wl.top_k)
     ws = torch.empty(lay.total, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    # A plain device copy of known size (256 MiB read + 256 MiB written), run
+    # before the timed region: rocprofv3 FETCH_SIZE / WRITE_SIZE counters read
+    # for it calibrate the counters read for the layer's kernels.
+    calib_src = torch.ones(COPY_CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
 
     print(f"# warmup {args.warmup}, timed {args.steps}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

@@ -391,11 +391,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) *reinterpret_cast<v4u*>(lds + buf * ABUF + adst[u]) = src[u];
   };
+  // Weight loads are unconditional: a wave past the end of N reloads the last
+  // column block (never used).  A branch around them would make the
+  // compiler's wait counts assume they may be missing and drain the prefetch.
+  const int64_t nb_last = p.N / 16 - 1;
   auto load_b = [&](int ks, uint4 (&b)[WN], uint32_t (&sc)[WN]) __attribute__((always_inline)) {
-    if (!cols) return;
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      const int64_t nb = nb0 + j;
+      const int64_t nb = min(nb0 + j, nb_last);
       b[j] = *reinterpret_cast<const uint4*>(wbase + ((nb * KS + ks) * 64 + lane) * 16);
       if (V == kInt4Fp8)
         sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS + ks) * 16 + (lane & 15)) * 4);
@@ -413,6 +416,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
     const int kp = min(ks + 2, KS - 1);
     load_a(kp, ast[S & 1]);
     load_b(kp, bq[(S + 2) & 3], sq[(S + 2) & 3]);
+    // keep the step's phases in order (prefetch | LDS reads + MFMAs | LDS
+    // writes + barrier) so the wait counts refer to the intended loads
+    __builtin_amdgcn_sched_barrier(0);
     const uint8_t* abuf = lds + (S & 1) * ABUF + (WM * wm) * 2048;
     v8i bop[WN];
 #pragma unroll
@@ -439,6 +445,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     // A of step ks+1 (a harmless copy of the last step once past the end)
     store_a((S + 1) & 1, ast[(S + 1) & 1]);
     __syncthreads();
