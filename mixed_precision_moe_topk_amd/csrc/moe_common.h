@@ -31,23 +31,20 @@ struct Tile {
   int32_t pad;
 };
 
-// Block -> (tile, N-tile) map shared by the GEMM kernels.  The hardware hands
-// consecutive workgroups to the 8 XCDs in turn, so block b runs on XCD b % 8;
-// each XCD gets a contiguous range of work items (item = tile * n_tiles +
-// N-tile), so all N-tiles of an M-tile run together on one XCD and its
-// activation rows are fetched into that XCD's L2 once.  The grid is a
-// multiple of 8 and covers every item once; blocks past the end return false.
+// Block -> (tile, N-tile) map shared by the GEMM kernels: block b takes work
+// item b, M-tile b / n_tiles and N-tile b % n_tiles.  The N-tiles of one
+// M-tile are neighbours in launch order, so the blocks resident at one time
+// share their activation rows in L2 and sweep the weight columns of an expert
+// together.  (An XCD-contiguous remap and grouped M-tile orders were measured
+// on the 16384-token DeepSeek-V4-shaped prefill: both fetched more bytes from
+// HBM and ran slower than this plain order.)  Blocks past the last item
+// return false.
 __device__ __forceinline__ bool work_item(const Tile* tiles, const int32_t* num_tiles,
                                           int32_t n_tiles, Tile* tile, int* nt) {
-  const int64_t total = (int64_t)(*num_tiles) * n_tiles;
-  const int64_t per = (total + 7) / 8;
-  const int64_t b = blockIdx.x;
-  if (b / 8 >= per) return false;
-  const int64_t item = (b % 8) * per + b / 8;
-  if (item >= total) return false;
-  const int64_t mt = item / n_tiles;
-  *nt = (int)(item - mt * n_tiles);
-  *tile = tiles[mt];
+  const int64_t item = blockIdx.x;
+  if (item >= (int64_t)(*num_tiles) * n_tiles) return false;
+  *nt = (int)(item % n_tiles);
+  *tile = tiles[item / n_tiles];
   return true;
 }
 
@@ -167,18 +164,19 @@ hipError_t launch_unpack(int wfmt_int4, const uint8_t* codes, int64_t codes_stri
 
 // GEMM tile configurations (rows x device columns per block tile), chosen by
 // the mean rows per expert.  BF16 activations keep the register-direct kernel;
-// E4M3 activations use the LDS-staged kernel for the two larger shapes.
+// E4M3 activations use the LDS-staged kernels for the two larger shapes (A in
+// LDS for 64 x 256, A and weights in LDS with 8 waves for 128 x 256).
 struct GemmCfg {
-  int waves_m, wm, wn;
+  int nw, waves_m, wm, wn;  // waves per block, wave rows, 16x16 tiles per wave (M, N)
   int bm() const { return 16 * waves_m * wm; }
-  int bn() const { return 16 * (4 / waves_m) * wn; }
+  int bn() const { return 16 * (nw / waves_m) * wn; }
 };
 constexpr int kNumGemmCfg = 3;
 inline GemmCfg gemm_cfg(int i, bool bf16) {
   switch (i) {
-    case 0: return GemmCfg{1, 1, 2};                                  // 16 x 128
-    case 1: return bf16 ? GemmCfg{1, 3, 2} : GemmCfg{1, 4, 4};        // 48 x 128 / 64 x 256
-    default: return GemmCfg{2, 4, 4};                                 // 128 x 128
+    case 0: return GemmCfg{4, 1, 1, 2};                                // 16 x 128
+    case 1: return bf16 ? GemmCfg{4, 1, 3, 2} : GemmCfg{4, 1, 4, 4};   // 48 x 128 / 64 x 256
+    default: return bf16 ? GemmCfg{4, 2, 4, 4} : GemmCfg{8, 2, 4, 4};  // 128 x 128 / 128 x 256
   }
 }
 

@@ -22,12 +22,16 @@
 // 4*(l/16)+[0,4).  For the unscaled paths any k permutation shared by both
 // operands gives the same sum, which the INT4 and bf16 paths use.
 //
-// Block = 4 waves (WAVES_M x WAVES_N); each wave owns WM x WN 16x16 output
+// Blocks of WAVES_M x WAVES_N waves; each wave owns WM x WN 16x16 output
 // tiles.  FC1 writes h = silu(gate) * up (gate/up rows interleaved per 16-row
 // block by the weight layout); FC2 writes y2 = acc * row scale.
 #include <type_traits>
 
 #include "moe_common.h"
+
+#ifndef MOE_INTERLEAVE
+#define MOE_INTERLEAVE 1
+#endif
 
 namespace moe {
 
@@ -300,9 +304,24 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
 }
 
 
+// Scheduling hint for one K step: NMFMA MFMAs with NVMEM global loads and NDS
+// LDS reads spread between them (two LDS reads first, for the first A
+// fragment).  Only ordering hints; no effect on results.
+template <int NMFMA, int NVMEM, int NDS>
+__device__ __forceinline__ void interleave_schedule() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+#pragma unroll
+  for (int m = 0; m < NMFMA; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if (m < NVMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+    if (m + 1 < NMFMA && (m + 1) * (NDS - 2) / NMFMA != m * (NDS - 2) / NMFMA)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+}
+
 // ----------------------------------------------------------------------------
 // LDS-staged grouped GEMM for E4M3 activations (MXFP4 x FP8, INT4 x FP8).
-// Block = 4 waves, WAVES_M x WAVES_N; each wave owns 16*WM rows and 16*WN
+// Block = NW waves, WAVES_M x WAVES_N; each wave owns 16*WM rows and 16*WN
 // device columns.  Per 128-wide K step the block stages the tile's A rows
 // (gathered token rows for FC1) into LDS in MFMA fragment order: fragment
 // (i, h) is 1 KB holding the 16-byte operand pieces of its 64 lanes; lane
@@ -313,22 +332,31 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
 // barrier per step.  Global loads run two steps ahead:
 // A into two register staging sets, weights (pre-shuffled, straight into the
 // MFMA operand registers) into four register sets, so a load has two steps of
-// MFMA work to arrive.  Rows past the tile end are loaded as copies of its
+// MFMA work to arrive.  An MXFP4 scale word covers four K steps (one E8M0 byte
+// per step), so it is loaded once per four steps.  Rows past the tile end are loaded as copies of its
 // last row and never stored; 16-row subtiles past the end are skipped.
-template <int V, bool FC1, int WAVES_M, int WM, int WN>
-__global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
+// Body of k_gemm_lds for one work item.  FULL: the tile has BM rows and the
+// wave's columns lie inside N (known per block), so every step is one basic
+// block: no per-subtile branches, which lets the scheduling hints interleave
+// MFMAs with the step's memory instructions.
+template <int V, bool FC1, int NW, int WAVES_M, int WM, int WN, int PB, int AD, bool FULL>
+__device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds, const Tile tile,
+                                              const int nt) {
+  static_assert(PB >= 1 && PB <= 3 && AD >= 2 && AD <= 4, "prefetch distances");
+  constexpr int NB = (PB == 1) ? 2 : 4;  // weight register sets (prefetch distance PB)
+  constexpr int AS = (AD == 2) ? 2 : 4;  // A staging register sets (prefetch distance AD)
+
   static_assert(V == kMxfp4Fp8 || V == kInt4Fp8, "E4M3 activations only");
   static_assert(!FC1 || WN % 2 == 0, "FC1 pairs gate/up tiles");
-  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int NT = kWave * NW;           // threads per block
+  constexpr int WAVES_N = NW / WAVES_M;
   constexpr int BM = 16 * WM * WAVES_M;
   static_assert(BM % 32 == 0, "BM must be a multiple of 32");
+  static_assert((BM * 8) % NT == 0, "A stage must split evenly over the threads");
   constexpr int ABUF = BM * kKStep;        // bytes of one A stage
-  constexpr int NCH = BM * 8 / 256;        // 16-byte chunks per thread per stage
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * ABUF];
+  constexpr int NCH = BM * 8 / NT;         // 16-byte chunks per thread per stage
+  constexpr bool MX = V == kMxfp4Fp8;
 
-  Tile tile;
-  int nt;
-  if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
   // wave-uniform values are made scalar so that branches on them are scalar
   // branches (exec-masked branches make the compiler drain every outstanding
   // load at each join, which would serialise the prefetch)
@@ -357,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
   int adst[NCH];
 #pragma unroll
   for (int u = 0; u < NCH; ++u) {
-    const int q = threadIdx.x + 256 * u;
+    const int q = threadIdx.x + NT * u;
     const int r = q >> 3, c = q & 7;
     const int rr = min(tile.row0 + r, row_end - 1);
     const int64_t src = FC1 ? (int64_t)p.row_token[rr] : (int64_t)rr;
@@ -379,9 +407,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  v4u ast[2][NCH];
-  uint4 bq[4][WN];
-  uint32_t sq[4][WN];
+  v4u ast[AS][NCH];
+  uint4 bq[NB][WN];
+  uint32_t sq[NB][WN];         // INT4 group scales, one set per B register set
+  uint32_t sx[WN], sx_next[WN];  // MXFP4 scale words of this / the next 4 steps
 
   auto load_a = [&](int ks, v4u (&dst)[NCH]) __attribute__((always_inline)) {
 #pragma unroll
@@ -400,10 +429,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
     for (int j = 0; j < WN; ++j) {
       const int64_t nb = min(nb0 + j, nb_last);
       b[j] = *reinterpret_cast<const uint4*>(wbase + ((nb * KS + ks) * 64 + lane) * 16);
-      if (V == kInt4Fp8)
+      if (!MX)
         sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS + ks) * 16 + (lane & 15)) * 4);
-      else
-        sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS4 + (ks >> 2)) * 64 + lane) * 4);
+    }
+  };
+  auto load_sx = [&](int ks, uint32_t (&sc)[WN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int64_t nb = min(nb0 + j, nb_last);
+      sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS4 + (ks >> 2)) * 64 + lane) * 4);
     }
   };
 
@@ -413,20 +447,28 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
   // operations and the compiler's wait counts stay exact.
   auto step = [&](auto s_c, int ks) __attribute__((always_inline)) {
     constexpr int S = decltype(s_c)::value;
-    const int kp = min(ks + 2, KS - 1);
-    load_a(kp, ast[S & 1]);
-    load_b(kp, bq[(S + 2) & 3], sq[(S + 2) & 3]);
+    // the scale words of steps ks..ks+3 were loaded PB steps ago
+    if constexpr (MX && S == 0) {
+#pragma unroll
+      for (int j = 0; j < WN; ++j) sx[j] = sx_next[j];
+    }
+    load_a(min(ks + AD, KS - 1), ast[(S + AD) % AS]);
+    load_b(min(ks + PB, KS - 1), bq[(S + PB) % NB], sq[(S + PB) % NB]);
+    constexpr bool LOAD_SX = MX && (S + PB) % 4 == 0;
+    if constexpr (LOAD_SX) load_sx(min(ks + PB, KS - 1), sx_next);
+#if !MOE_INTERLEAVE
     // keep the step's phases in order (prefetch | LDS reads + MFMAs | LDS
     // writes + barrier) so the wait counts refer to the intended loads
     __builtin_amdgcn_sched_barrier(0);
+#endif
     const uint8_t* abuf = lds + (S & 1) * ABUF + (WM * wm) * 2048;
     v8i bop[WN];
 #pragma unroll
     for (int j = 0; j < WN; ++j)
-      bop[j] = (V == kMxfp4Fp8) ? fp4_operand(bq[S][j]) : int4_operand(bq[S][j]);
+      bop[j] = (V == kMxfp4Fp8) ? fp4_operand(bq[S % NB][j]) : int4_operand(bq[S % NB][j]);
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
-      if (cols && i < nvalid) {
+      if (FULL || (cols && i < nvalid)) {
         const uint4 lo = *reinterpret_cast<const uint4*>(abuf + (2 * i) * 1024 + rd0);
         const uint4 hi = *reinterpret_cast<const uint4*>(abuf + (2 * i) * 1024 + rd1);
         const v8i aop = as_v8i(lo, hi);
@@ -434,27 +476,46 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
         for (int j = 0; j < WN; ++j) {
           if (V == kMxfp4Fp8) {
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                aop, bop[j], acc[i][j], 0, 4, 0, 127, S, (int)sq[S][j]);
+                aop, bop[j], acc[i][j], 0, 4, 0, 127, S, (int)sx[j]);
           } else {
             const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 aop, bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-            const float gs = __uint_as_float(sq[S][j]);
+            const float gs = __uint_as_float(sq[S % NB][j]);
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[i][j][v] += part[v] * gs;
           }
         }
       }
     }
+#if MOE_INTERLEAVE
+    // issue order inside the step: the wave's global loads and LDS reads are
+    // spread between its MFMAs so they issue while the matrix pipe is busy
+    if (FULL) interleave_schedule<WM * WN, (MX ? (LOAD_SX ? 2 : 1) : 2) * WN + NCH, 2 * WM>();
+#endif
     __builtin_amdgcn_sched_barrier(0);
     // A of step ks+1 (a harmless copy of the last step once past the end)
-    store_a((S + 1) & 1, ast[(S + 1) & 1]);
+    store_a((S + 1) & 1, ast[(S + 1) % AS]);
     __syncthreads();
   };
 
+  // Prologue loads in step order.  The fences keep the scheduler from sinking
+  // the first step's weight loads behind later ones: the wait counts at the
+  // loop head are the minimum over the entry and back-edge paths, so a late
+  // load here would tighten every iteration's waits.
   load_a(0, ast[0]);
   load_b(0, bq[0], sq[0]);
-  load_a(min(1, KS - 1), ast[1]);
-  load_b(min(1, KS - 1), bq[1], sq[1]);
+  if (MX) load_sx(0, sx_next);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 1; i < AD; ++i) {
+    load_a(min(i, KS - 1), ast[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 1; i < PB; ++i) {
+    load_b(min(i, KS - 1), bq[i], sq[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   store_a(0, ast[0]);
   __syncthreads();
   int ks = 0;
@@ -470,20 +531,250 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams p) {
   epilogue<FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
+template <int V, bool FC1, int NW, int WAVES_M, int WM, int WN, int MINB = 2, int PB = 2,
+          int AD = 2>
+__global__ __launch_bounds__(kWave * NW, MINB) void k_gemm_lds(GemmParams p) {
+  constexpr int BM = 16 * WM * WAVES_M;
+  constexpr int BN = 16 * WN * (NW / WAVES_M);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BM * kKStep];
+  Tile tile;
+  int nt;
+  if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
+  const bool full = tile.nrows == BM && (int64_t)(nt + 1) * BN <= p.N;
+  if (full) gemm_lds_body<V, FC1, NW, WAVES_M, WM, WN, PB, AD, true>(p, lds, tile, nt);
+  else gemm_lds_body<V, FC1, NW, WAVES_M, WM, WN, PB, AD, false>(p, lds, tile, nt);
+}
+
+// Scheduling hint for one K step of the two-operand LDS kernel: the step's
+// weight fragments and first activation fragment are read first, then the
+// MFMAs with the remaining LDS reads and the global loads spread between them.
+template <int NMFMA, int NVMEM, int NDS_FIRST, int NDS_REST>
+__device__ __forceinline__ void interleave_schedule_ab() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NDS_FIRST, 0);  // DS read
+#pragma unroll
+  for (int m = 0; m < NMFMA; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if (m < NVMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+    if (m + 1 < NMFMA && (m + 1) * NDS_REST / NMFMA != m * NDS_REST / NMFMA)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Grouped GEMM with both operands staged through LDS (E4M3 activations).
+// Block = NW waves, WAVES_M x WAVES_N, each wave 16*WM rows x 16*WN device
+// columns; block tile BM x BN.  A per-thread global load carries at most one
+// 16-byte chunk of the step's A tile or weight tile, so every weight byte
+// reaches the CU once per block instead of once per wave row, which halves
+// the global-load bytes per MFMA against register-direct weights (the vector
+// memory path, not HBM, bounds the prefill GEMMs).  Per 128-wide K step and
+// LDS stage: A in the swizzled fragment order of gemm_lds_body, then the
+// block's weight fragments in their device order (16-column block b at
+// b * 1 KB, lane l's 16 bytes at l * 16: reads and writes are conflict-free).
+// Two stages, one barrier per step; global loads run two steps ahead through
+// two register staging sets.  MXFP4 scale words (one per four steps) and INT4
+// group scales go straight to registers.
+template <int V, bool FC1, int NW, int WAVES_M, int WM, int WN, bool FULL>
+__device__ __forceinline__ void gemm_ab_body(const GemmParams& p, uint8_t* lds, const Tile tile,
+                                             const int nt) {
+  static_assert(V == kMxfp4Fp8 || V == kInt4Fp8, "E4M3 activations only");
+  static_assert(!FC1 || WN % 2 == 0, "FC1 pairs gate/up tiles");
+  constexpr int NT = kWave * NW;
+  constexpr int WAVES_N = NW / WAVES_M;
+  constexpr int BM = 16 * WM * WAVES_M;
+  constexpr int BNB = WAVES_N * WN;        // 16-column blocks per block tile
+  constexpr int ABUF = BM * kKStep;        // A bytes of one stage
+  constexpr int SBUF = ABUF + BNB * 1024;  // bytes of one stage
+  constexpr int NCA = BM * 8 / NT;         // A chunks per thread per step
+  constexpr int NCB = BNB * 64 / NT;       // weight chunks per thread per step
+  static_assert(NCA * NT == BM * 8 && NCB * NT == BNB * 64, "chunks must split evenly");
+  static_assert(128 % (16 * WN) == 0, "wave columns must tile 128");
+  constexpr bool MX = V == kMxfp4Fp8;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = lane_id();
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int row_end = tile.row0 + tile.nrows;
+  const int row_base = tile.row0 + 16 * WM * wm;
+  const int nvalid = __builtin_amdgcn_readfirstlane(max(0, min(WM, (row_end - row_base + 15) / 16)));
+
+  const int K = p.K;
+  const int KS = K / kKStep, KS4 = (KS + 3) / 4;
+  const int64_t e = tile.expert;
+  const uint8_t* wbase = p.w + e * p.w_expert_stride;
+  const uint8_t* sbase = p.s + e * p.s_expert_stride;
+  const int64_t nbb = (int64_t)nt * BNB;   // first 16-column block of the tile
+  const int64_t nb0 = nbb + wn * WN;       // first 16-column block of this wave
+  const bool cols = __builtin_amdgcn_readfirstlane((int)(nb0 * 16 < p.N)) != 0;
+  const int jvalid = cols ? WN : 0;
+  const int64_t nb_last = p.N / 16 - 1;
+
+  // A chunks: tile row r, 16-byte column chunk c (as in gemm_lds_body)
+  const uint8_t* asrc[NCA];
+  int adst[NCA];
+#pragma unroll
+  for (int u = 0; u < NCA; ++u) {
+    const int q = threadIdx.x + NT * u;
+    const int r = q >> 3, c = q & 7;
+    const int rr = min(tile.row0 + r, row_end - 1);
+    const int64_t src = FC1 ? (int64_t)p.row_token[rr] : (int64_t)rr;
+    asrc[u] = p.a + src * p.a_stride + 16 * c;
+    int g, h;
+    if (MX) { g = c & 3; h = c >> 2; }
+    else { g = c >> 1; h = c & 1; }
+    const int rho = r & 15;
+    adst[u] = ((r >> 4) * 2 + h) * 1024 + (16 * g + (rho ^ ((2 * g + h) | ((rho & 1) << 3)))) * 16;
+  }
+  // weight chunks: chunk q is lane slot q % 64 of local 16-column block q / 64
+  // (blocks past N reload the last block; their columns are never used)
+  const uint8_t* bsrc[NCB];
+#pragma unroll
+  for (int u = 0; u < NCB; ++u) {
+    const int q = threadIdx.x + NT * u;
+    const int64_t nb = min(nbb + (q >> 6), nb_last);
+    bsrc[u] = wbase + (nb * KS * 64 + (q & 63)) * 16;
+  }
+  const int rho_l = lane & 15, g_l = lane >> 4;
+  const int rd0 = (16 * g_l + (rho_l ^ ((2 * g_l) | ((rho_l & 1) << 3)))) * 16;
+  const int rd1 = 1024 + (16 * g_l + (rho_l ^ ((2 * g_l + 1) | ((rho_l & 1) << 3)))) * 16;
+  const int rdb = ABUF + wn * WN * 1024 + lane * 16;
+
+  v4f acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  v4u ast[2][NCA], bst[2][NCB];
+  uint32_t sq[4][WN];            // INT4 group scales of steps ks .. ks+3 (mod 4)
+  uint32_t sx[WN], sx_next[WN];  // MXFP4 scale words of this / the next 4 steps
+
+  auto load_ab = [&](int ks, v4u (&da)[NCA], v4u (&db)[NCB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NCA; ++u) da[u] = *reinterpret_cast<const v4u*>(asrc[u] + ks * kKStep);
+#pragma unroll
+    for (int u = 0; u < NCB; ++u) db[u] = *reinterpret_cast<const v4u*>(bsrc[u] + ks * 1024);
+  };
+  auto store_ab = [&](int buf, const v4u (&sa)[NCA], const v4u (&sb)[NCB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NCA; ++u) *reinterpret_cast<v4u*>(lds + buf * SBUF + adst[u]) = sa[u];
+#pragma unroll
+    for (int u = 0; u < NCB; ++u)
+      *reinterpret_cast<v4u*>(lds + buf * SBUF + ABUF + (threadIdx.x + NT * u) * 16) = sb[u];
+  };
+  auto load_sq = [&](int ks, uint32_t (&sc)[WN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int64_t nb = min(nb0 + j, nb_last);
+      sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS + ks) * 16 + (lane & 15)) * 4);
+    }
+  };
+  auto load_sx = [&](int ks, uint32_t (&sc)[WN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int64_t nb = min(nb0 + j, nb_last);
+      sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS4 + (ks >> 2)) * 64 + lane) * 4);
+    }
+  };
+
+  auto step = [&](auto s_c, int ks) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_c)::value;
+    if constexpr (MX && S == 0) {
+#pragma unroll
+      for (int j = 0; j < WN; ++j) sx[j] = sx_next[j];
+    }
+    const int kp = min(ks + 2, KS - 1);
+    load_ab(kp, ast[S & 1], bst[S & 1]);
+    if constexpr (!MX) load_sq(kp, sq[(S + 2) % 4]);
+    constexpr bool LOAD_SX = MX && (S + 2) % 4 == 0;
+    if constexpr (LOAD_SX) load_sx(kp, sx_next);
+    const uint8_t* sbuf = lds + (S & 1) * SBUF;
+    v8i bop[WN];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const uint4 b = *reinterpret_cast<const uint4*>(sbuf + rdb + j * 1024);
+      bop[j] = MX ? fp4_operand(b) : int4_operand(b);
+    }
+    const uint8_t* abuf = sbuf + (WM * wm) * 2048;
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      if (FULL || (cols && i < nvalid)) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(abuf + (2 * i) * 1024 + rd0);
+        const uint4 hi = *reinterpret_cast<const uint4*>(abuf + (2 * i) * 1024 + rd1);
+        const v8i aop = as_v8i(lo, hi);
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          if (MX) {
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                aop, bop[j], acc[i][j], 0, 4, 0, 127, S, (int)sx[j]);
+          } else {
+            const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                aop, bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+            const float gs = __uint_as_float(sq[S][j]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[i][j][v] += part[v] * gs;
+          }
+        }
+      }
+    }
+    if (FULL)
+      interleave_schedule_ab<WM * WN, NCA + NCB + (MX ? (LOAD_SX ? WN : 0) : WN), WN + 2,
+                             2 * WM - 2>();
+    __builtin_amdgcn_sched_barrier(0);
+    // operands of step ks+1 (harmless copies of the last step once past the end)
+    store_ab((S + 1) & 1, ast[(S + 1) & 1], bst[(S + 1) & 1]);
+    __syncthreads();
+  };
+
+  // prologue loads in step order (fenced: see gemm_lds_body)
+  load_ab(0, ast[0], bst[0]);
+  if (MX) load_sx(0, sx_next);
+  else load_sq(0, sq[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  load_ab(min(1, KS - 1), ast[1], bst[1]);
+  if (!MX) load_sq(min(1, KS - 1), sq[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  store_ab(0, ast[0], bst[0]);
+  __syncthreads();
+  int ks = 0;
+  for (; ks + 4 <= KS; ks += 4) {
+    step(std::integral_constant<int, 0>{}, ks);
+    step(std::integral_constant<int, 1>{}, ks + 1);
+    step(std::integral_constant<int, 2>{}, ks + 2);
+    step(std::integral_constant<int, 3>{}, ks + 3);
+  }
+  if (ks < KS) step(std::integral_constant<int, 0>{}, ks);
+  if (ks + 1 < KS) step(std::integral_constant<int, 1>{}, ks + 1);
+  if (ks + 2 < KS) step(std::integral_constant<int, 2>{}, ks + 2);
+  epilogue<FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+}
+
+template <int V, bool FC1, int NW, int WAVES_M, int WM, int WN, int MINB = 1>
+__global__ __launch_bounds__(kWave * NW, MINB) void k_gemm_ab(GemmParams p) {
+  constexpr int BM = 16 * WM * WAVES_M;
+  constexpr int BN = 16 * WN * (NW / WAVES_M);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (BM * kKStep + BN * 64)];
+  Tile tile;
+  int nt;
+  if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
+  const bool full = tile.nrows == BM && (int64_t)(nt + 1) * BN <= p.N;
+  if (full) gemm_ab_body<V, FC1, NW, WAVES_M, WM, WN, true>(p, lds, tile, nt);
+  else gemm_ab_body<V, FC1, NW, WAVES_M, WM, WN, false>(p, lds, tile, nt);
+}
+
 template <int V, bool FC1>
 static hipError_t launch_v(int cfg, const GemmParams& p, int64_t max_tiles, hipStream_t st) {
-  const int64_t blocks = (max_tiles * p.n_tiles + 7) / 8 * 8;  // work_item needs a multiple of 8
+  const int64_t blocks = max_tiles * p.n_tiles;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   switch (cfg) {
     case 0: k_gemm<V, FC1, 1, 1, 2><<<(unsigned)blocks, 256, 0, st>>>(p); break;
     case 1:
       if constexpr (V == kMxfp4Bf16) k_gemm<V, FC1, 1, 3, 2><<<(unsigned)blocks, 256, 0, st>>>(p);
-      else k_gemm_lds<V, FC1, 1, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p);
+      else k_gemm_lds<V, FC1, 4, 1, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p);
       break;
     default:
       if constexpr (V == kMxfp4Bf16) k_gemm<V, FC1, 2, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p);
-      else k_gemm_lds<V, FC1, 2, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p);
+      else k_gemm_ab<V, FC1, 8, 2, 4, 4><<<(unsigned)blocks, 512, 0, st>>>(p);
       break;
   }
   return hipGetLastError();

@@ -17,6 +17,8 @@ SMALL = [
     (300, 5, 2, 256, 384, "mxfp4", "fp8", 14, 0.0),   # 120 rows/expert -> 128-row tiles, tails
     (300, 5, 2, 256, 384, "int4", "fp8", 15, 2.0),
     (300, 5, 2, 256, 384, "mxfp4", "bf16", 16, 2.0),
+    (400, 4, 2, 384, 384, "mxfp4", "fp8", 21, 0.0),   # 200 rows/expert, full + ragged tiles, N tail
+    (400, 4, 2, 384, 640, "int4", "fp8", 22, 1.0),
     (9, 40, 4, 512, 128, "mxfp4", "fp8", 17, 0.0),    # <1 row/expert -> 16-row tiles, empties
     (9, 40, 4, 512, 128, "mxfp4", "bf16", 18, 0.0),
     (9, 40, 4, 512, 128, "int4", "fp8", 19, 0.0),
