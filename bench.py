@@ -41,24 +41,31 @@ METRIC = "fused-MoE tokens/s + % MFMA peak (prefill) / % HBM GB/s (decode), 1 GP
 ORACLE_SAMPLE_TOKENS = {"tiny_mxfp4_fp8": 16, "dsv3_decode_mxfp4_bf16": 10,
                         "dsv3_prefill_mxfp4_fp8": 6, "dsv4pro_prefill_mxfp4_fp8": 6,
                         "dsv3_int4_fp8": 6}
-GEMM_SOURCES = ("mixed_precision_moe_topk_amd/csrc/moe_gemm.hip",
-                "mixed_precision_moe_topk_amd/csrc/moe_common.h")
+CSRC = "mixed_precision_moe_topk_amd/csrc/"
 
 
-def measured_traffic(workload):
-    """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE, scaled by a calibration copy), or None when no
-    summary exists or the GEMM source has changed since it was taken."""
+def gemm_source_sha256(afmt, cfg):
+    """SHA-256 of the sources of the GEMM kernel that runs for this activation
+    format and tile configuration (16-row tiles and BF16 activations use the
+    register-direct kernel, the rest the LDS-staged kernels)."""
     import hashlib
 
+    kfile = "moe_gemm_direct.hip" if (cfg == 0 or afmt == "bf16") else "moe_gemm_lds.hip"
+    h = hashlib.sha256()
+    for f in (kfile, "moe_gemm_common.h", "moe_common.h"):
+        h.update(open(os.path.join(ROOT, CSRC + f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, source_sha):
+    """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a calibration copy), or None when no
+    summary exists or the kernel's source has changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"gemm1_{workload}.traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in GEMM_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if h.hexdigest() != rec.get("gemm_source_sha256"):
+    if rec.get("gemm_source_sha256") != source_sha:
         return None
     return float(rec["traffic_bytes_per_launch"])
 
@@ -177,19 +184,21 @@ def main():
     gemm1_bytes = active * (w1_codes + w1_scales)
     gemm1_flops = 2.0 * rows * 2 * wl.inter * wl.hidden
     g1_s = stage_avg["gemm1"] / 1e3
+    src_sha = gemm_source_sha256(wl.afmt, lay.gemm_cfg)
     if wl.regime in ("hbm", "latency"):
         achieved = gemm1_bytes / g1_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(wl.key)}
+                "traffic": measured_traffic(wl.key, src_sha)}
     else:
         achieved = gemm1_flops / g1_s / 1e12
         peak = MFMA_PEAK_TFLOPS[wl.afmt]
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": measured_traffic(wl.key)}
+                "traffic": measured_traffic(wl.key, src_sha)}
     roof["kernel"] = "gemm1"
     roof["kernel_ms"] = round(stage_avg["gemm1"], 4)
+    roof["kernel_source_sha256"] = src_sha
     roof["algorithmic_bytes"] = gemm1_bytes if wl.regime in ("hbm", "latency") else None
     roof["algorithmic_flops"] = gemm1_flops
 

@@ -1,0 +1,159 @@
+// Operand helpers and epilogue shared by the grouped GEMM kernels of the fused
+// MoE on CDNA4 matrix cores (gfx950).
+//
+// flashinfer PR #3738 ("perf: optimize MXFP4xBF16 & INT4xFP8 and add MXFP4xFP8
+// CUTLASS MoE backend for SM90"), Description and Implementation Notes: grouped
+// MoE GEMMs over MXFP4 or INT4 expert weights against FP8 or BF16 activations,
+// a precomputed work map, per-token-scale epilogues, and (for MXFP4 x FP8) the
+// E8M0 weight scale applied inside the matrix product.  On gfx950 the block-
+// scaled MFMA V_MFMA_SCALE_F32_16X16X128_F8F6F4 takes E2M1 weights and E8M0
+// scales directly, so no pre-MMA scale folding is needed:
+//   * MXFP4 x FP8 : scaled MFMA, A = E4M3 token codes (scale 1), B = E2M1
+//                   weights with their E8M0 scales; the token scale is applied
+//                   in the epilogue.
+//   * MXFP4 x BF16: weights expanded to bf16 in registers with the E8M0 scale
+//                   folded in (exact), then bf16 MFMA 16x16x32.
+//   * INT4 x FP8  : INT4 codes mapped to E4M3 (exact) in registers, one FP8
+//                   MFMA per 128-element group, then the group's float32 scale
+//                   multiplies the partial sum (post-MMA scaling).
+// Operand lane layouts (16x16x128): an FP8 operand lane l holds row l%16 with
+// bytes 0-15 at k = 16*(l/16)+b and bytes 16-31 at k = 64+16*(l/16)+(b-16); an
+// FP4 operand lane holds 32 consecutive k = 32*(l/16)+n; E8M0 scale of lane l
+// covers row l%16, k-block l/16; the output lane l holds column l%16 of rows
+// 4*(l/16)+[0,4).  For the unscaled paths any k permutation shared by both
+// operands gives the same sum, which the INT4 and bf16 paths use.
+//
+// Blocks of WAVES_M x WAVES_N waves; each wave owns WM x WN 16x16 output
+// tiles.  FC1 writes h = silu(gate) * up (gate/up rows interleaved per 16-row
+// block by the weight layout); FC2 writes y2 = acc * row scale.
+#pragma once
+
+#include <type_traits>
+
+#include "moe_common.h"
+
+namespace moe {
+
+template <int V>
+struct Frag;
+
+template <>
+struct Frag<kMxfp4Fp8> {
+  static constexpr int kA = 2;  // uint4 per A row fragment
+};
+template <>
+struct Frag<kInt4Fp8> {
+  static constexpr int kA = 2;
+};
+template <>
+struct Frag<kMxfp4Bf16> {
+  static constexpr int kA = 4;
+};
+
+__device__ __forceinline__ v8i as_v8i(const uint4& lo, const uint4& hi) {
+  v8i r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+__device__ __forceinline__ v8i fp4_operand(const uint4& b) {
+  v8i r;
+  r[0] = b.x; r[1] = b.y; r[2] = b.z; r[3] = b.w;
+  r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+  return r;
+}
+
+__device__ __forceinline__ v8i int4_operand(const uint4& b) {
+  const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+  v8i r;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    r[2 * d] = int4sm_to_e4m3(w[d] & 0x0F0F0F0Fu);
+    r[2 * d + 1] = int4sm_to_e4m3((w[d] >> 4) & 0x0F0F0F0Fu);
+  }
+  return r;
+}
+
+__device__ __forceinline__ v8bf as_bf16x8(const uint4& u) {
+  v8bf r;
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[2 * i] = __builtin_bit_cast(__bf16, (unsigned short)(w[i] & 0xFFFF));
+    r[2 * i + 1] = __builtin_bit_cast(__bf16, (unsigned short)(w[i] >> 16));
+  }
+  return r;
+}
+
+// 8 E2M1 codes (one dword) -> 8 bf16 values times `scale` (exact conversion).
+__device__ __forceinline__ v8bf fp4x8_to_bf16(uint32_t w, float scale) {
+  v8bf r;
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// Epilogue shared by the GEMM kernels.  Output tile (i, j) of a wave holds, in
+// lane l, column 16*(nb0+j) + l%16 of rows row_base + 16*i + 4*(l/16) + [0, 4).
+//   FC1: tiles (2q, 2q+1) are the gate and up halves of intermediate block
+//        (nb0 + 2q)/2; h = silu(g*s) * (u*s), s = token scale.
+//   FC2: y2 = acc * s, s = row scale.
+template <bool FC1, int WM, int WN>
+__device__ __forceinline__ void epilogue(const GemmParams& p, const v4f (&acc)[WM][WN],
+                                         int row_base, int row_end, int nvalid, int64_t nb0,
+                                         int jvalid, int lane) {
+  const int col_lane = lane & 15;
+  const int row_lane = 4 * (lane >> 4);
+  if (FC1) {
+#pragma unroll
+    for (int q = 0; q < WN / 2; ++q) {
+      if (2 * q >= jvalid) continue;
+      const int64_t ib = (nb0 + 2 * q) >> 1;  // intermediate 16-column block
+      const int64_t c = ib * 16 + col_lane;
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        if (i >= nvalid) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = row_base + 16 * i + row_lane + v;
+          if (r < row_end) {
+            const float s = p.row_scale ? p.row_scale[p.row_token[r]] : 1.0f;
+            const float g = acc[i][2 * q][v] * s;
+            const float u = acc[i][2 * q + 1][v] * s;
+            p.out[(int64_t)r * p.out_stride + c] = g / (1.0f + expf(-g)) * u;
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      if (j >= jvalid) continue;
+      const int64_t c = (nb0 + j) * 16 + col_lane;
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        if (i >= nvalid) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = row_base + 16 * i + row_lane + v;
+          if (r < row_end) {
+            const float s = p.row_scale ? p.row_scale[r] : 1.0f;
+            p.out[(int64_t)r * p.out_stride + c] = acc[i][j][v] * s;
+          }
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_gemm_direct(int variant, bool fc1, int cfg, const GemmParams& p,
+                              int64_t max_tiles, hipStream_t st);
+hipError_t launch_gemm_lds(int variant, bool fc1, int cfg, const GemmParams& p,
+                           int64_t max_tiles, hipStream_t st);
+
+}  // namespace moe

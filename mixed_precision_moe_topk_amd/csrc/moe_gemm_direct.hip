@@ -1,0 +1,197 @@
+// Register-direct grouped GEMM of the fused MoE (gfx950): each wave loads its
+// own activation and weight fragments straight into MFMA operand registers,
+// one K step ahead.  Used for BF16 activations (the weights are expanded from
+// E2M1 to bf16 in registers with the E8M0 scale folded in) and for the 16-row
+// tiles of decode-sized batches, where the weight stream from HBM dominates.
+#include "moe_gemm_common.h"
+
+namespace moe {
+
+// Block = 4 waves, WAVES_M x (4 / WAVES_M); each wave owns WM x WN 16x16
+// output tiles.
+template <int V, bool FC1, int WAVES_M, int WM, int WN>
+__global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
+  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int NA = Frag<V>::kA;
+  static_assert(!FC1 || WN % 2 == 0, "FC1 pairs gate/up tiles");
+  Tile tile;
+  int nt;
+  if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int row_base = tile.row0 + 16 * WM * wm;
+  const int row_end = tile.row0 + tile.nrows;
+  const int nvalid = min(WM, (row_end - row_base + 15) / 16);
+  if (nvalid <= 0) return;
+
+  const int K = p.K;
+  const int KS = K / kKStep, KS4 = (KS + 3) / 4;
+  const int64_t e = tile.expert;
+  const uint8_t* wbase = p.w + e * p.w_expert_stride;
+  const uint8_t* sbase = p.s + e * p.s_expert_stride;
+  const int64_t nb0 = (int64_t)nt * (WAVES_N * WN) + wn * WN;
+  const int jvalid = (int)min<int64_t>(WN, p.N / 16 - nb0);  // N tail: 16-column blocks left
+  if (jvalid <= 0) return;
+
+  // A row pointers (rows past the tile end re-read its last row; their
+  // outputs are never stored)
+  const uint8_t* arow[WM];
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+    const int r = min(row_base + 16 * i + (lane & 15), row_end - 1);
+    const int64_t src = FC1 ? (int64_t)p.row_token[r] : (int64_t)r;
+    int64_t off;
+    if (V == kMxfp4Fp8) off = 16 * (lane >> 4);
+    else if (V == kInt4Fp8) off = 32 * (lane >> 4);
+    else off = 64 * (lane >> 4);  // bf16: 32 elements * 2 bytes
+    arow[i] = p.a + src * p.a_stride + off;
+  }
+
+  v4f acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  uint4 ac[WM][NA], an[WM][NA];
+  uint4 bc[WN], bn[WN];
+  uint32_t scc[WN], scn[WN];  // E8M0 dword (MXFP4) or float bits (INT4 group scale)
+
+  auto load = [&](int ks, uint4 (&a)[WM][NA], uint4 (&b)[WN], uint32_t (&sc)[WN]) {
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      if (i < nvalid) {
+        if (V == kMxfp4Fp8) {
+          a[i][0] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep);
+          a[i][1] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep + 64);
+        } else if (V == kInt4Fp8) {
+          a[i][0] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep);
+          a[i][1] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep + 16);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            a[i][q] = *reinterpret_cast<const uint4*>(arow[i] + 2 * ks * kKStep + 16 * q);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      if (j >= jvalid) continue;
+      const int64_t nb = nb0 + j;
+      b[j] = *reinterpret_cast<const uint4*>(wbase + ((nb * KS + ks) * 64 + lane) * 16);
+      if (V == kInt4Fp8)
+        sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS + ks) * 16 + (lane & 15)) * 4);
+      else
+        sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS4 + (ks >> 2)) * 64 + lane) * 4);
+    }
+  };
+
+  auto compute = [&](int ks, const uint4 (&a)[WM][NA], const uint4 (&b)[WN],
+                     const uint32_t (&sc)[WN]) {
+    if (V == kMxfp4Fp8) {
+      v8i bop[WN];
+#pragma unroll
+      for (int j = 0; j < WN; ++j) bop[j] = fp4_operand(b[j]);
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        if (i < nvalid) {
+          const v8i aop = as_v8i(a[i][0], a[i][1]);
+#pragma unroll
+          for (int j = 0; j < WN; ++j) {
+            if (j >= jvalid) continue;
+            switch (ks & 3) {
+              case 0: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, 127, 0, (int)sc[j]); break;
+              case 1: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, 127, 1, (int)sc[j]); break;
+              case 2: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, 127, 2, (int)sc[j]); break;
+              default: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, 127, 3, (int)sc[j]); break;
+            }
+          }
+        }
+      }
+    } else if (V == kInt4Fp8) {
+      v8i bop[WN];
+#pragma unroll
+      for (int j = 0; j < WN; ++j) bop[j] = int4_operand(b[j]);
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        if (i < nvalid) {
+          const v8i aop = as_v8i(a[i][0], a[i][1]);
+#pragma unroll
+          for (int j = 0; j < WN; ++j) {
+            if (j >= jvalid) continue;
+            const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                aop, bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+            const float gs = __uint_as_float(sc[j]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[i][j][v] += part[v] * gs;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        if (j >= jvalid) continue;
+        const float scale = e8m0_to_float((sc[j] >> (8 * (ks & 3))) & 0xFFu);
+        const uint32_t bw[4] = {b[j].x, b[j].y, b[j].z, b[j].w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const v8bf bop = fp4x8_to_bf16(bw[s], scale);
+#pragma unroll
+          for (int i = 0; i < WM; ++i) {
+            if (i < nvalid)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[i][s]), bop,
+                                                                  acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+
+  load(0, ac, bc, scc);
+  for (int ks = 0; ks < KS; ks += 2) {
+    if (ks + 1 < KS) load(ks + 1, an, bn, scn);
+    compute(ks, ac, bc, scc);
+    if (ks + 1 < KS) {
+      if (ks + 2 < KS) load(ks + 2, ac, bc, scc);
+      compute(ks + 1, an, bn, scn);
+    }
+  }
+
+  epilogue<FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+}
+
+
+template <int V, bool FC1>
+static hipError_t launch_v(int cfg, const GemmParams& p, int64_t blocks, hipStream_t st) {
+  switch (cfg) {
+    case 0: k_gemm<V, FC1, 1, 1, 2><<<(unsigned)blocks, 256, 0, st>>>(p); break;
+    case 1: k_gemm<V, FC1, 1, 3, 2><<<(unsigned)blocks, 256, 0, st>>>(p); break;
+    default: k_gemm<V, FC1, 2, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_direct(int variant, bool fc1, int cfg, const GemmParams& p,
+                              int64_t max_tiles, hipStream_t st) {
+  const int64_t blocks = max_tiles * p.n_tiles;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  switch (variant) {
+    case kMxfp4Fp8: return fc1 ? launch_v<kMxfp4Fp8, true>(cfg, p, blocks, st)
+                               : launch_v<kMxfp4Fp8, false>(cfg, p, blocks, st);
+    case kMxfp4Bf16: return fc1 ? launch_v<kMxfp4Bf16, true>(cfg, p, blocks, st)
+                                : launch_v<kMxfp4Bf16, false>(cfg, p, blocks, st);
+    default: return fc1 ? launch_v<kInt4Fp8, true>(cfg, p, blocks, st)
+                        : launch_v<kInt4Fp8, false>(cfg, p, blocks, st);
+  }
+}
+
+// Tile configuration -> kernel: the register-direct kernel for 16-row tiles
+// and BF16 activations, the LDS-staged kernels otherwise.
+hipError_t launch_gemm(int variant, bool fc1, int cfg, const GemmParams& p, int64_t max_tiles,
+                       hipStream_t st) {
+  if (cfg == 0 || variant == kMxfp4Bf16) return launch_gemm_direct(variant, fc1, cfg, p, max_tiles, st);
+  return launch_gemm_lds(variant, fc1, cfg, p, max_tiles, st);
+}
+
+}  // namespace moe
