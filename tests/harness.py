@@ -96,6 +96,8 @@ class Problem:
         r["y2"] = view(L.y2, np.float32, rows * wl.hidden).reshape(rows, wl.hidden)
         r["num_tiles"] = int(view(L.num_tiles, np.int32, 1)[0])
         r["tile_m"] = L.tile_m
+        tl = view(L.tiles, np.int32, 4 * L.max_tiles).reshape(-1, 4)
+        r["tiles"] = tl[:r["num_tiles"], :3].copy()
         return r
 
     def unpack(self, first: int, count: int):
@@ -125,11 +127,22 @@ class Problem:
         return O.forward(hb, lg, wl.top_k, lambda e: self.oracle_w[e], wl.wfmt, wl.afmt)
 
 
+def expected_work_map(offsets, tile_m):
+    """GEMM work map from the per-expert row ranges: (expert, row0, nrows) of
+    every tile, in expert order; each expert's rows are cut into tile_m-row
+    tiles, the last one partial."""
+    tiles = [(e, int(offsets[e]) + r, min(tile_m, int(offsets[e + 1] - offsets[e]) - r))
+             for e in range(len(offsets) - 1)
+             for r in range(0, int(offsets[e + 1] - offsets[e]), tile_m)]
+    return np.array(tiles, np.int32).reshape(-1, 3)
+
+
 def compare_all(g, r, wl, exact_rows=True):
     """Stage-by-stage comparison of GPU results g with oracle results r."""
     assert np.array_equal(g["ids"], r["ids"]), "routing ids differ"
     assert np.max(np.abs(g["weights"] - r["weights"])) <= 1e-6
     assert np.array_equal(g["offsets"], r["offsets"].astype(np.int32))
+    assert np.array_equal(g["tiles"], expected_work_map(r["offsets"], g["tile_m"])), "work map differs"
     if exact_rows:
         assert np.array_equal(g["row_token"], r["row_token"].astype(np.int32))
         assert np.array_equal(g["slot_row"], r["slot_row"].astype(np.int32))

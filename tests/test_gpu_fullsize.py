@@ -12,7 +12,7 @@ import pytest
 import moe_inputs as MI
 import oracle as O
 from oracle import formats as F
-from tests.harness import Problem, check_output, rel_l2
+from tests.harness import Problem, check_output, expected_work_map, rel_l2
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -70,6 +70,8 @@ def test_fullsize_sampled(name):
     assert np.array_equal(g["offsets"], off.astype(np.int32))
     assert np.array_equal(g["row_token"], tok.astype(np.int32))
     assert np.array_equal(g["slot_row"], slot_row.astype(np.int32))
+    # GEMM work map (main and tail tiles) from the expert row ranges
+    assert np.array_equal(g["tiles"], expected_work_map(off, g["tile_m"]))
     # per-token E4M3 codes and scales for every token
     if wl.afmt == "fp8":
         q, s = O.quant.e4m3_rows(F.bf16_to_f32(p.hidden))
