@@ -138,7 +138,7 @@ moe_status layout_of(const moe_dims* d, int64_t T, int32_t k, moe_ws_layout* L) 
     return fail(MOE_ERR_INVALID_ARG, "num_tokens %lld too large", (long long)T);
   const int64_t E = d->num_experts, H = d->hidden, I = d->inter;
   const int cfg = pick_cfg(rows, d->num_experts);
-  const int tile_m = moe::gemm_cfg(cfg, d->afmt == MOE_A_BF16).bm();
+  const int tile_m = moe::gemm_cfg(cfg, variant_of(d)).bm();
   const int64_t nchunks = cdiv(T, moe::kRouteChunkTokens);
   const int64_t max_tiles = cdiv(rows, tile_m) + std::min<int64_t>(E, rows);
   size_t off = 0;
@@ -408,7 +408,7 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
   trace_mark(tc, 2, stream);
 
   const int variant = variant_of(dims);
-  const moe::GemmCfg cfg = moe::gemm_cfg(L.gemm_cfg, !fp8);
+  const moe::GemmCfg cfg = moe::gemm_cfg(L.gemm_cfg, variant);
   const uint8_t* wbytes = static_cast<const uint8_t*>(weights);
   const uint8_t* sbytes = static_cast<const uint8_t*>(scales);
   float* h = reinterpret_cast<float*>(ws + L.h);

@@ -164,19 +164,25 @@ hipError_t launch_unpack(int wfmt_int4, const uint8_t* codes, int64_t codes_stri
 
 // GEMM tile configurations (rows x device columns per block tile), chosen by
 // the mean rows per expert.  BF16 activations keep the register-direct kernel;
-// E4M3 activations use the LDS-staged kernels for the two larger shapes (A in
-// LDS for 64 x 256, A and weights in LDS with 8 waves for 128 x 256).
+// E4M3 activations use the LDS-staged kernels for the two larger shapes: A in
+// LDS for 64 x 256; for 128-row tiles both operands in LDS with 8 waves,
+// filled by direct-to-LDS loads for MXFP4 (128 x 512) and through registers
+// for INT4 (128 x 256, whose E4M3 expansion of the weights needs the
+// registers the larger tile would take).
 struct GemmCfg {
   int nw, waves_m, wm, wn;  // waves per block, wave rows, 16x16 tiles per wave (M, N)
   int bm() const { return 16 * waves_m * wm; }
   int bn() const { return 16 * (nw / waves_m) * wn; }
 };
 constexpr int kNumGemmCfg = 3;
-inline GemmCfg gemm_cfg(int i, bool bf16) {
+inline GemmCfg gemm_cfg(int i, int variant) {
   switch (i) {
-    case 0: return GemmCfg{4, 1, 1, 2};                                // 16 x 128
-    case 1: return bf16 ? GemmCfg{4, 1, 3, 2} : GemmCfg{4, 1, 4, 4};   // 48 x 128 / 64 x 256
-    default: return bf16 ? GemmCfg{4, 2, 4, 4} : GemmCfg{8, 2, 4, 4};  // 128 x 128 / 128 x 256
+    case 0: return GemmCfg{4, 1, 1, 2};                                        // 16 x 128
+    case 1: return variant == kMxfp4Bf16 ? GemmCfg{4, 1, 3, 2} : GemmCfg{4, 1, 4, 4};  // 48 x 128 / 64 x 256
+    default:
+      return variant == kMxfp4Bf16 ? GemmCfg{4, 2, 4, 4}     // 128 x 128
+             : variant == kMxfp4Fp8 ? GemmCfg{8, 2, 4, 8}   // 128 x 512
+                                    : GemmCfg{8, 2, 4, 4};  // 128 x 256
   }
 }
 

@@ -466,9 +466,213 @@ __global__ __launch_bounds__(kWave * NW, MINB) void k_gemm_ab(GemmParams p) {
   else gemm_ab_body<V, FC1, NW, WAVES_M, WM, WN, false>(p, lds, tile, nt);
 }
 
+// ----------------------------------------------------------------------------
+// Direct-to-LDS grouped GEMM for E4M3 activations, 128 x 512 block tiles.
+// 8 waves (2 x 4), each 64 rows x 128 device columns (4 x 8 MFMA tiles), so
+// one K step reads 16 KB of operands from LDS per 32 MFMAs per wave (a third
+// less LDS traffic per MFMA than 64 x 64 wave tiles, which were LDS-bound).
+// Operands reach LDS by global_load_lds (16 bytes per lane, lane L of a wave
+// instruction lands at M0 + 16 L; an SALU write of M0 needs one wait state
+// before the load reads it), so no staging registers are needed:
+//   A       2 stages x 16 KB  fragment (g, h) of 16-row group g at (2g+h) KB,
+//                             lane L's 16-byte operand piece at 16 L
+//   weights 3 stages x 32 KB  16-column block b at b KB, in device order
+//   scales  MXFP4: 2 slots x 8 KB (one 4-step group each), block b at 256 b;
+//           INT4: 3 stages x 2 KB (one step each), block b at 64 b
+// Step ks issues A of ks+1, weights (and INT4 scales) of ks+2 and, at the
+// start of a 4-step group, the next group's MXFP4 scale words; the wave then
+// waits until its loads of step ks+1 have landed (the vector memory counter
+// counts these loads in issue order) and joins the block barrier.  Every
+// load's step index is clamped to the last step, so the number of loads per
+// step, and with it every wait count, is fixed.  The loads are inline
+// assembly: the compiler does not track them, which keeps its conservative
+// full drains out of the loop; the kernel drains them itself before the
+// epilogue (an LDS write landing after the block exits would corrupt the next
+// block's LDS).
+namespace dma {
+constexpr int kNW = 8, kWM = 4, kWN = 8, kWavesN = 4;
+constexpr int kBM = 128, kBNB = 32;  // rows, 16-column blocks per block tile
+constexpr int kABuf = kBM * kKStep, kBBuf = kBNB * 1024;
+constexpr int kAOff = 0, kBOff = 2 * kABuf, kSOff = kBOff + 3 * kBBuf;
+constexpr int kSxSlot = kBNB * 256, kSqStage = kBNB * 64;
+constexpr int lds_bytes(bool mx) { return kSOff + (mx ? 2 * kSxSlot : 3 * kSqStage); }
+}  // namespace dma
+
+__device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gaddr), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* gaddr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(gaddr), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4_s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+// Wait until at most N of this wave's loads are outstanding, then block barrier.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+template <int V, bool FC1, bool FULL>
+__device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds, const Tile tile,
+                                              const int nt) {
+  using namespace dma;
+  static_assert(V == kMxfp4Fp8 || V == kInt4Fp8, "E4M3 activations only");
+  constexpr bool MX = V == kMxfp4Fp8;
+  constexpr int WM = kWM, WN = kWN;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = lane_id();
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  const int row_end = tile.row0 + tile.nrows;
+  const int row_base = tile.row0 + 16 * WM * wm;
+  const int nvalid = __builtin_amdgcn_readfirstlane(max(0, min(WM, (row_end - row_base + 15) / 16)));
+  const int K = p.K;
+  const int KS = K / kKStep, KS4 = (KS + 3) / 4;
+  const int64_t e = tile.expert;
+  const uint8_t* wbase = p.w + e * p.w_expert_stride;
+  const uint8_t* sbase = p.s + e * p.s_expert_stride;
+  const int64_t nbb = (int64_t)nt * kBNB;
+  const int64_t nb0 = nbb + wn * WN;
+  const bool cols = __builtin_amdgcn_readfirstlane((int)(nb0 * 16 < p.N)) != 0;
+  const int jvalid = cols ? WN : 0;
+  const int64_t nb_last = p.N / 16 - 1;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+
+  // A: this wave loads fragments (wave, 0) and (wave, 1): row 16 wave + L%16
+  // of the tile (the last row repeated past the end), operand piece L/16
+  const int ar = min(tile.row0 + 16 * wave + (lane & 15), row_end - 1);
+  const uint8_t* arow = p.a + (FC1 ? (int64_t)p.row_token[ar] : (int64_t)ar) * p.a_stride +
+                        (MX ? 16 * (lane >> 4) : 32 * (lane >> 4));
+  constexpr int kAHalf = MX ? 64 : 16;  // k offset of the second operand half
+  // weights: this wave loads 16-column blocks 4 wave + u, u < 4 (clamped to N)
+  const uint8_t* wcol[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) wcol[u] = wbase + min(nbb + 4 * wave + u, nb_last) * KS * 1024;
+  // INT4 scales: lane L loads column L%16 of block 4 wave + L/16
+  const uint8_t* qcol = sbase + (min(nbb + 4 * wave + (lane >> 4), nb_last) * KS * 16 + (lane & 15)) * 4;
+
+  auto issue_a = [&](int ks, int stage) __attribute__((always_inline)) {
+    const uint32_t dst = lds0 + kAOff + stage * kABuf + wave * 2048;
+    lds_dma16(arow + ks * kKStep, dst);
+    lds_dma16(arow + ks * kKStep + kAHalf, dst + 1024);
+  };
+  auto issue_b = [&](int ks, int stage) __attribute__((always_inline)) {
+    const uint32_t dst = lds0 + kBOff + stage * kBBuf + wave * 4096;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) lds_dma16_s(wcol[u] + ks * 1024, lane * 16, dst + u * 1024);
+    if (!MX) lds_dma4(qcol + ks * 64, lds0 + kSOff + stage * kSqStage + wave * 256);
+  };
+  auto issue_sx = [&](int grp, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint8_t* src = sbase + (min(nbb + 4 * wave + u, nb_last) * KS4 + grp) * 256;
+      lds_dma4_s(src, lane * 4, lds0 + kSOff + slot * kSxSlot + (wave * 4 + u) * 256);
+    }
+  };
+
+  v4f acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint32_t sx[WN];
+
+  // loads per step after the A loads: weights (4), INT4 scales (1), and at
+  // the start of a group the MXFP4 scale words (4)
+  auto step = [&](auto s_c, int ks, int bstage) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_c)::value;
+    issue_a(min(ks + 1, KS - 1), (S + 1) & 1);
+    issue_b(min(ks + 2, KS - 1), bstage == 0 ? 2 : bstage - 1);
+    if constexpr (MX && S == 0) issue_sx(min((ks >> 2) + 1, KS4 - 1), ((ks >> 2) + 1) & 1);
+    const uint8_t* bs = lds + kBOff + bstage * kBBuf + (wn * WN) * 1024 + lane * 16;
+    if constexpr (MX && S == 0) {
+      const uint8_t* ss = lds + kSOff + ((ks >> 2) & 1) * kSxSlot + (wn * WN) * 256 + lane * 4;
+#pragma unroll
+      for (int j = 0; j < WN; ++j) sx[j] = *reinterpret_cast<const uint32_t*>(ss + j * 256);
+    }
+    float gs[WN];
+    if constexpr (!MX) {
+      const uint8_t* qs = lds + kSOff + bstage * kSqStage + (wn * WN) * 64 + (lane & 15) * 4;
+#pragma unroll
+      for (int j = 0; j < WN; ++j) gs[j] = *reinterpret_cast<const float*>(qs + j * 64);
+    }
+    v8i bop[WN];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
+      bop[j] = MX ? fp4_operand(b) : int4_operand(b);
+    }
+    const uint8_t* as = lds + kAOff + (S & 1) * kABuf + (wm * WM) * 2048 + lane * 16;
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      if (FULL || (cols && i < nvalid)) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(as + i * 2048);
+        const uint4 hi = *reinterpret_cast<const uint4*>(as + i * 2048 + 1024);
+        const v8i aop = as_v8i(lo, hi);
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          if constexpr (MX) {
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                aop, bop[j], acc[i][j], 0, 4, 0, 127, S, (int)sx[j]);
+          } else {
+            const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                aop, bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[i][j][v] += part[v] * gs[j];
+          }
+        }
+      }
+    }
+    // the loads of step ks+1 (A issued above, weights one step earlier) have
+    // landed once only the loads issued after this step's A loads remain
+    wait_barrier<(MX ? (S == 0 ? 8 : 4) : 5)>();
+  };
+
+  // prologue: A and weights (and scales) of step 0, weights of step 1
+  issue_a(0, 0);
+  issue_b(0, 0);
+  if (MX) issue_sx(0, 0);
+  issue_b(min(1, KS - 1), 1);
+  wait_barrier<(MX ? 4 : 5)>();
+  int ks = 0, bstage = 0;
+  for (; ks + 4 <= KS; ks += 4) {
+    step(std::integral_constant<int, 0>{}, ks, bstage);
+    bstage = bstage == 2 ? 0 : bstage + 1;
+    step(std::integral_constant<int, 1>{}, ks + 1, bstage);
+    bstage = bstage == 2 ? 0 : bstage + 1;
+    step(std::integral_constant<int, 2>{}, ks + 2, bstage);
+    bstage = bstage == 2 ? 0 : bstage + 1;
+    step(std::integral_constant<int, 3>{}, ks + 3, bstage);
+    bstage = bstage == 2 ? 0 : bstage + 1;
+  }
+  if (ks < KS) { step(std::integral_constant<int, 0>{}, ks, bstage); bstage = bstage == 2 ? 0 : bstage + 1; }
+  if (ks + 1 < KS) { step(std::integral_constant<int, 1>{}, ks + 1, bstage); bstage = bstage == 2 ? 0 : bstage + 1; }
+  if (ks + 2 < KS) step(std::integral_constant<int, 2>{}, ks + 2, bstage);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  epilogue<FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+}
+
+template <int V, bool FC1>
+__global__ __launch_bounds__(dma::kNW * kWave, 1) void k_gemm_dma(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[dma::lds_bytes(V == kMxfp4Fp8)];
+  Tile tile;
+  int nt;
+  if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
+  const bool full = tile.nrows == dma::kBM && (int64_t)(nt + 1) * dma::kBNB * 16 <= p.N;
+  if (full) gemm_dma_body<V, FC1, true>(p, lds, tile, nt);
+  else gemm_dma_body<V, FC1, false>(p, lds, tile, nt);
+}
+
 template <int V, bool FC1>
 static hipError_t launch_v(int cfg, const GemmParams& p, int64_t blocks, hipStream_t st) {
   if (cfg == 1) k_gemm_lds<V, FC1, 4, 1, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p);
+  else if constexpr (V == kMxfp4Fp8) k_gemm_dma<V, FC1><<<(unsigned)blocks, dma::kNW * kWave, 0, st>>>(p);
   else k_gemm_ab<V, FC1, 8, 2, 4, 4><<<(unsigned)blocks, 512, 0, st>>>(p);
   return hipGetLastError();
 }
