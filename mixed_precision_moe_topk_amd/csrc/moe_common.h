@@ -165,8 +165,8 @@ hipError_t launch_unpack(int wfmt_int4, const uint8_t* codes, int64_t codes_stri
 // GEMM tile configurations (rows x device columns per block tile), chosen by
 // the mean rows per expert.  BF16 activations keep the register-direct kernel;
 // E4M3 activations use the LDS-staged kernels for the two larger shapes: A in
-// LDS for 64 x 256; for 128-row tiles both operands in LDS with 8 waves,
-// filled by direct-to-LDS loads for MXFP4 (128 x 512) and through registers
+// LDS for 64 x 256; for the largest shape both operands in LDS with 8 waves,
+// filled by direct-to-LDS loads for MXFP4 (160 x 512) and through registers
 // for INT4 (128 x 256, whose E4M3 expansion of the weights needs the
 // registers the larger tile would take).
 struct GemmCfg {
@@ -181,7 +181,7 @@ inline GemmCfg gemm_cfg(int i, int variant) {
     case 1: return variant == kMxfp4Bf16 ? GemmCfg{4, 1, 3, 2} : GemmCfg{4, 1, 4, 4};  // 48 x 128 / 64 x 256
     default:
       return variant == kMxfp4Bf16 ? GemmCfg{4, 2, 4, 4}     // 128 x 128
-             : variant == kMxfp4Fp8 ? GemmCfg{8, 2, 4, 8}   // 128 x 512
+             : variant == kMxfp4Fp8 ? GemmCfg{8, 2, 5, 8}   // 160 x 512
                                     : GemmCfg{8, 2, 4, 4};  // 128 x 256
   }
 }

@@ -467,19 +467,22 @@ __global__ __launch_bounds__(kWave * NW, MINB) void k_gemm_ab(GemmParams p) {
 }
 
 // ----------------------------------------------------------------------------
-// Direct-to-LDS grouped GEMM for E4M3 activations, 128 x 512 block tiles.
-// 8 waves (2 x 4), each 64 rows x 128 device columns (4 x 8 MFMA tiles), so
-// one K step reads 16 KB of operands from LDS per 32 MFMAs per wave (a third
-// less LDS traffic per MFMA than 64 x 64 wave tiles, which were LDS-bound).
+// Direct-to-LDS grouped GEMM for MXFP4 x FP8, 160 x 512 block tiles.
+// 8 waves (2 x 4), each 80 rows x 128 device columns (5 x 8 MFMA tiles), so
+// one K step reads 18 KB of operands from LDS per 40 MFMAs per wave (40%
+// less LDS traffic per MFMA than 64 x 64 wave tiles).  160-row tiles
+// let one tile hold an expert of up to 160 rows: a tile costs about the same
+// whether full or not (its weight stream dominates), so fewer tiles per
+// expert is what counts.
 // Operands reach LDS by global_load_lds (16 bytes per lane, lane L of a wave
 // instruction lands at M0 + 16 L; an SALU write of M0 needs one wait state
 // before the load reads it), so no staging registers are needed:
-//   A       2 stages x 16 KB  fragment (g, h) of 16-row group g at (2g+h) KB,
+//   A       2 stages x 20 KB  fragment (g, h) of 16-row group g at (2g+h) KB,
 //                             lane L's 16-byte operand piece at 16 L
 //   weights 3 stages x 32 KB  16-column block b at b KB, in device order
-//   scales  MXFP4: 2 slots x 8 KB (one 4-step group each), block b at 256 b;
-//           INT4: 3 stages x 2 KB (one step each), block b at 64 b
-// Step ks issues A of ks+1, weights (and INT4 scales) of ks+2 and, at the
+//   scales  2 slots x 8 KB (one 4-step group of E8M0 words each), block b
+//           at 256 b
+// Step ks issues A of ks+1, weights of ks+2 and, at the
 // start of a 4-step group, the next group's MXFP4 scale words; the wave then
 // waits until its loads of step ks+1 have landed (the vector memory counter
 // counts these loads in issue order) and joins the block barrier.  Every
@@ -490,12 +493,16 @@ __global__ __launch_bounds__(kWave * NW, MINB) void k_gemm_ab(GemmParams p) {
 // epilogue (an LDS write landing after the block exits would corrupt the next
 // block's LDS).
 namespace dma {
-constexpr int kNW = 8, kWM = 4, kWN = 8, kWavesN = 4;
-constexpr int kBM = 128, kBNB = 32;  // rows, 16-column blocks per block tile
+constexpr int kNW = 8, kWM = 5, kWN = 8, kWavesN = 4;
+constexpr int kBM = 2 * 16 * kWM, kBNB = kWavesN * kWN;  // rows, 16-column blocks per tile
+constexpr int kRG = kBM / 16;           // 16-row groups (wave w loads w and w + 8)
+constexpr int kBPW = kBNB / kNW;        // weight blocks loaded per wave
+static_assert(kRG >= kNW && kRG <= 2 * kNW, "row groups per wave");
+static_assert(kBPW * kNW == kBNB, "weight blocks per wave");
 constexpr int kABuf = kBM * kKStep, kBBuf = kBNB * 1024;
 constexpr int kAOff = 0, kBOff = 2 * kABuf, kSOff = kBOff + 3 * kBBuf;
-constexpr int kSxSlot = kBNB * 256, kSqStage = kBNB * 64;
-constexpr int lds_bytes(bool mx) { return kSOff + (mx ? 2 * kSxSlot : 3 * kSqStage); }
+constexpr int kSxSlot = kBNB * 256;
+constexpr int kLdsBytes = kSOff + 2 * kSxSlot;
 }  // namespace dma
 
 __device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_addr) {
@@ -505,10 +512,6 @@ __device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_addr) 
 __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(const void* gaddr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(gaddr), "s"(lds_addr) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_dma4_s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
@@ -520,12 +523,14 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
-template <int V, bool FC1, bool FULL>
+// One code path for full and partial tiles: the per-subtile checks are scalar
+// branches, which also keep the compiler from hoisting every fragment read of
+// a step (a branch-free full-tile path needed more than 256 registers here).
+template <int V, bool FC1>
 __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds, const Tile tile,
                                               const int nt) {
   using namespace dma;
-  static_assert(V == kMxfp4Fp8 || V == kInt4Fp8, "E4M3 activations only");
-  constexpr bool MX = V == kMxfp4Fp8;
+  static_assert(V == kMxfp4Fp8, "MXFP4 weights x E4M3 activations only");
   constexpr int WM = kWM, WN = kWN;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = lane_id();
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -544,35 +549,40 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   const int64_t nb_last = p.N / 16 - 1;
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
 
-  // A: this wave loads fragments (wave, 0) and (wave, 1): row 16 wave + L%16
-  // of the tile (the last row repeated past the end), operand piece L/16
-  const int ar = min(tile.row0 + 16 * wave + (lane & 15), row_end - 1);
-  const uint8_t* arow = p.a + (FC1 ? (int64_t)p.row_token[ar] : (int64_t)ar) * p.a_stride +
-                        (MX ? 16 * (lane >> 4) : 32 * (lane >> 4));
-  constexpr int kAHalf = MX ? 64 : 16;  // k offset of the second operand half
-  // weights: this wave loads 16-column blocks 4 wave + u, u < 4 (clamped to N)
-  const uint8_t* wcol[4];
+  // A: this wave loads fragments (g, 0) and (g, 1) of row groups g = wave and
+  // (waves below kRG - 8) g = wave + 8: row 16 g + L%16 of the tile (the
+  // last row repeated past the end), operand piece L/16
+  const bool two_rg = wave < kRG - kNW;  // compile-time false when kRG == kNW
+  const int kofs = 16 * (lane >> 4);
+  const int ar0 = min(tile.row0 + 16 * wave + (lane & 15), row_end - 1);
+  const int ar1 = min(tile.row0 + 16 * (wave + kNW) + (lane & 15), row_end - 1);
+  const uint8_t* arow0 = p.a + (FC1 ? (int64_t)p.row_token[ar0] : (int64_t)ar0) * p.a_stride + kofs;
+  const uint8_t* arow1 = p.a + (FC1 ? (int64_t)p.row_token[ar1] : (int64_t)ar1) * p.a_stride + kofs;
+  constexpr int kAHalf = 64;  // k offset of the second operand half
+  // weights: this wave loads 16-column blocks kBPW wave + u (clamped to N)
+  const uint8_t* wcol[kBPW];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) wcol[u] = wbase + min(nbb + 4 * wave + u, nb_last) * KS * 1024;
-  // INT4 scales: lane L loads column L%16 of block 4 wave + L/16
-  const uint8_t* qcol = sbase + (min(nbb + 4 * wave + (lane >> 4), nb_last) * KS * 16 + (lane & 15)) * 4;
+  for (int u = 0; u < kBPW; ++u) wcol[u] = wbase + min(nbb + kBPW * wave + u, nb_last) * KS * 1024;
 
   auto issue_a = [&](int ks, int stage) __attribute__((always_inline)) {
     const uint32_t dst = lds0 + kAOff + stage * kABuf + wave * 2048;
-    lds_dma16(arow + ks * kKStep, dst);
-    lds_dma16(arow + ks * kKStep + kAHalf, dst + 1024);
+    lds_dma16(arow0 + ks * kKStep, dst);
+    lds_dma16(arow0 + ks * kKStep + kAHalf, dst + 1024);
+    if (two_rg) {
+      lds_dma16(arow1 + ks * kKStep, dst + kNW * 2048);
+      lds_dma16(arow1 + ks * kKStep + kAHalf, dst + kNW * 2048 + 1024);
+    }
   };
   auto issue_b = [&](int ks, int stage) __attribute__((always_inline)) {
-    const uint32_t dst = lds0 + kBOff + stage * kBBuf + wave * 4096;
+    const uint32_t dst = lds0 + kBOff + stage * kBBuf + wave * kBPW * 1024;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) lds_dma16_s(wcol[u] + ks * 1024, lane * 16, dst + u * 1024);
-    if (!MX) lds_dma4(qcol + ks * 64, lds0 + kSOff + stage * kSqStage + wave * 256);
+    for (int u = 0; u < kBPW; ++u) lds_dma16_s(wcol[u] + ks * 1024, lane * 16, dst + u * 1024);
   };
   auto issue_sx = [&](int grp, int slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint8_t* src = sbase + (min(nbb + 4 * wave + u, nb_last) * KS4 + grp) * 256;
-      lds_dma4_s(src, lane * 4, lds0 + kSOff + slot * kSxSlot + (wave * 4 + u) * 256);
+    for (int u = 0; u < kBPW; ++u) {
+      const uint8_t* src = sbase + (min(nbb + kBPW * wave + u, nb_last) * KS4 + grp) * 256;
+      lds_dma4_s(src, lane * 4, lds0 + kSOff + slot * kSxSlot + (wave * kBPW + u) * 256);
     }
   };
 
@@ -583,63 +593,49 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
     for (int j = 0; j < WN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   uint32_t sx[WN];
 
-  // loads per step after the A loads: weights (4), INT4 scales (1), and at
-  // the start of a group the MXFP4 scale words (4)
+  // loads per step after the A loads (which come first, 2 or 4 per wave):
+  // weights (kBPW) and, at the start of a group, the scale words (kBPW)
   auto step = [&](auto s_c, int ks, int bstage) __attribute__((always_inline)) {
     constexpr int S = decltype(s_c)::value;
     issue_a(min(ks + 1, KS - 1), (S + 1) & 1);
     issue_b(min(ks + 2, KS - 1), bstage == 0 ? 2 : bstage - 1);
-    if constexpr (MX && S == 0) issue_sx(min((ks >> 2) + 1, KS4 - 1), ((ks >> 2) + 1) & 1);
+    if constexpr (S == 0) issue_sx(min((ks >> 2) + 1, KS4 - 1), ((ks >> 2) + 1) & 1);
     const uint8_t* bs = lds + kBOff + bstage * kBBuf + (wn * WN) * 1024 + lane * 16;
-    if constexpr (MX && S == 0) {
+    if constexpr (S == 0) {
       const uint8_t* ss = lds + kSOff + ((ks >> 2) & 1) * kSxSlot + (wn * WN) * 256 + lane * 4;
 #pragma unroll
       for (int j = 0; j < WN; ++j) sx[j] = *reinterpret_cast<const uint32_t*>(ss + j * 256);
-    }
-    float gs[WN];
-    if constexpr (!MX) {
-      const uint8_t* qs = lds + kSOff + bstage * kSqStage + (wn * WN) * 64 + (lane & 15) * 4;
-#pragma unroll
-      for (int j = 0; j < WN; ++j) gs[j] = *reinterpret_cast<const float*>(qs + j * 64);
     }
     v8i bop[WN];
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
       const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
-      bop[j] = MX ? fp4_operand(b) : int4_operand(b);
+      bop[j] = fp4_operand(b);
     }
     const uint8_t* as = lds + kAOff + (S & 1) * kABuf + (wm * WM) * 2048 + lane * 16;
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
-      if (FULL || (cols && i < nvalid)) {
+      if (cols && i < nvalid) {
         const uint4 lo = *reinterpret_cast<const uint4*>(as + i * 2048);
         const uint4 hi = *reinterpret_cast<const uint4*>(as + i * 2048 + 1024);
         const v8i aop = as_v8i(lo, hi);
 #pragma unroll
-        for (int j = 0; j < WN; ++j) {
-          if constexpr (MX) {
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                aop, bop[j], acc[i][j], 0, 4, 0, 127, S, (int)sx[j]);
-          } else {
-            const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                aop, bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[i][j][v] += part[v] * gs[j];
-          }
-        }
+        for (int j = 0; j < WN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              aop, bop[j], acc[i][j], 0, 4, 0, 127, S, (int)sx[j]);
       }
     }
     // the loads of step ks+1 (A issued above, weights one step earlier) have
     // landed once only the loads issued after this step's A loads remain
-    wait_barrier<(MX ? (S == 0 ? 8 : 4) : 5)>();
+    wait_barrier<(S == 0 ? 2 * kBPW : kBPW)>();
   };
 
   // prologue: A and weights (and scales) of step 0, weights of step 1
   issue_a(0, 0);
   issue_b(0, 0);
-  if (MX) issue_sx(0, 0);
+  issue_sx(0, 0);
   issue_b(min(1, KS - 1), 1);
-  wait_barrier<(MX ? 4 : 5)>();
+  wait_barrier<kBPW>();
   int ks = 0, bstage = 0;
   for (; ks + 4 <= KS; ks += 4) {
     step(std::integral_constant<int, 0>{}, ks, bstage);
@@ -660,13 +656,11 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
 
 template <int V, bool FC1>
 __global__ __launch_bounds__(dma::kNW * kWave, 1) void k_gemm_dma(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[dma::lds_bytes(V == kMxfp4Fp8)];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[dma::kLdsBytes];
   Tile tile;
   int nt;
   if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
-  const bool full = tile.nrows == dma::kBM && (int64_t)(nt + 1) * dma::kBNB * 16 <= p.N;
-  if (full) gemm_dma_body<V, FC1, true>(p, lds, tile, nt);
-  else gemm_dma_body<V, FC1, false>(p, lds, tile, nt);
+  gemm_dma_body<V, FC1>(p, lds, tile, nt);
 }
 
 template <int V, bool FC1>

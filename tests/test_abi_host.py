@@ -94,5 +94,5 @@ def test_workspace_layout_regions(L):
             lay.fc2_scales, lay.y2]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay.y2 + 4096 * 8 * 7168 * 4 <= lay.total
-    assert lay.tile_m == 128 and lay.gemm_cfg == 2
+    assert lay.tile_m == 160 and lay.gemm_cfg == 2
     assert M.workspace_layout(_d(), 64, 8).tile_m == 16
