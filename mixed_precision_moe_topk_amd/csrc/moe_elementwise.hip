@@ -25,40 +25,64 @@ __device__ __forceinline__ float block_max256(float v, float* red) {
   return v;
 }
 
+__device__ __forceinline__ float bf16x8_amax(const uint4& u, float amax) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    amax = fmaxf(amax, fabsf(__uint_as_float(w[j] << 16)));
+    amax = fmaxf(amax, fabsf(__uint_as_float(w[j] & 0xFFFF0000u)));
+  }
+  return amax;
+}
+
+__device__ __forceinline__ uint2 bf16x8_to_e4m3(const uint4& u, float s) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  uint32_t c[2] = {0, 0};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = e4m3_encode(__fdiv_rn(__uint_as_float(w[j] << 16), s));
+    const uint32_t hi = e4m3_encode(__fdiv_rn(__uint_as_float(w[j] & 0xFFFF0000u), s));
+    c[j / 2] |= (lo | (hi << 8)) << (16 * (j & 1));
+  }
+  return make_uint2(c[0], c[1]);
+}
+
 // One block per token row: x bf16 [T, H] -> codes E4M3 [T, H], scales [T].
-// H % 8 == 0.
+// H % 8 == 0.  Rows of up to 8192 elements are read once and kept in
+// registers between the amax and the quantisation; longer rows are read twice.
 __global__ __launch_bounds__(256) void k_quant_tokens(const uint16_t* __restrict__ x, int32_t H,
                                                       uint8_t* __restrict__ codes,
                                                       float* __restrict__ scales) {
   __shared__ float red[4];
+  constexpr int kR = 4;  // uint4 (8 bf16) per thread kept in registers
   const int64_t t = blockIdx.x;
   const uint4* row = reinterpret_cast<const uint4*>(x + t * H);
+  uint2* out = reinterpret_cast<uint2*>(codes + t * H);
   const int nv = H / 8;
   float amax = 0.0f;
-  for (int i = threadIdx.x; i < nv; i += blockDim.x) {
-    const uint4 u = row[i];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  if (nv <= kR * 256) {
+    uint4 u[kR];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      amax = fmaxf(amax, fabsf(__uint_as_float(w[j] << 16)));
-      amax = fmaxf(amax, fabsf(__uint_as_float(w[j] & 0xFFFF0000u)));
+    for (int r = 0; r < kR; ++r) {
+      const int i = threadIdx.x + 256 * r;
+      u[r] = i < nv ? row[i] : make_uint4(0, 0, 0, 0);
     }
+#pragma unroll
+    for (int r = 0; r < kR; ++r) amax = bf16x8_amax(u[r], amax);
+    amax = block_max256(amax, red);
+    const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int i = threadIdx.x + 256 * r;
+      if (i < nv) out[i] = bf16x8_to_e4m3(u[r], s);
+    }
+    if (threadIdx.x == 0) scales[t] = s;
+    return;
   }
+  for (int i = threadIdx.x; i < nv; i += blockDim.x) amax = bf16x8_amax(row[i], amax);
   amax = block_max256(amax, red);
   const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-  uint2* out = reinterpret_cast<uint2*>(codes + t * H);
-  for (int i = threadIdx.x; i < nv; i += blockDim.x) {
-    const uint4 u = row[i];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-    uint32_t c[2] = {0, 0};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = e4m3_encode(__fdiv_rn(__uint_as_float(w[j] << 16), s));
-      const uint32_t hi = e4m3_encode(__fdiv_rn(__uint_as_float(w[j] & 0xFFFF0000u), s));
-      c[j / 2] |= (lo | (hi << 8)) << (16 * (j & 1));
-    }
-    out[i] = make_uint2(c[0], c[1]);
-  }
+  for (int i = threadIdx.x; i < nv; i += blockDim.x) out[i] = bf16x8_to_e4m3(row[i], s);
   if (threadIdx.x == 0) scales[t] = s;
 }
 
@@ -83,40 +107,80 @@ __global__ __launch_bounds__(256) void k_requant(const float* __restrict__ h, in
     if (threadIdx.x == 0) scales[r] = 1.0f;
     return;
   }
+  auto f4_amax = [](const float4& v, float a) {
+    return fmaxf(fmaxf(a, fabsf(v.x)), fmaxf(fabsf(v.y), fmaxf(fabsf(v.z), fabsf(v.w))));
+  };
+  auto f4_e4m3 = [](const float4& v, float s) {
+    return e4m3_encode(__fdiv_rn(v.x, s)) | (e4m3_encode(__fdiv_rn(v.y, s)) << 8) |
+           (e4m3_encode(__fdiv_rn(v.z, s)) << 16) | (e4m3_encode(__fdiv_rn(v.w, s)) << 24);
+  };
+  uint32_t* out = reinterpret_cast<uint32_t*>(codes + r * I);
   float amax = 0.0f;
-  for (int i = threadIdx.x; i < nv; i += blockDim.x) {
-    const float4 v = row[i];
-    amax = fmaxf(fmaxf(amax, fabsf(v.x)), fmaxf(fabsf(v.y), fmaxf(fabsf(v.z), fabsf(v.w))));
+  constexpr int kR = 4;  // float4 per thread kept in registers (rows up to 4096)
+  if (nv <= kR * 256) {
+    float4 v[kR];
+#pragma unroll
+    for (int q = 0; q < kR; ++q) {
+      const int i = threadIdx.x + 256 * q;
+      v[q] = i < nv ? row[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < kR; ++q) amax = f4_amax(v[q], amax);
+    amax = block_max256(amax, red);
+    const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+#pragma unroll
+    for (int q = 0; q < kR; ++q) {
+      const int i = threadIdx.x + 256 * q;
+      if (i < nv) out[i] = f4_e4m3(v[q], s);
+    }
+    if (threadIdx.x == 0) scales[r] = s;
+    return;
   }
+  for (int i = threadIdx.x; i < nv; i += blockDim.x) amax = f4_amax(row[i], amax);
   amax = block_max256(amax, red);
   const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-  uint32_t* out = reinterpret_cast<uint32_t*>(codes + r * I);
-  for (int i = threadIdx.x; i < nv; i += blockDim.x) {
-    const float4 v = row[i];
-    out[i] = e4m3_encode(__fdiv_rn(v.x, s)) | (e4m3_encode(__fdiv_rn(v.y, s)) << 8) |
-             (e4m3_encode(__fdiv_rn(v.z, s)) << 16) | (e4m3_encode(__fdiv_rn(v.w, s)) << 24);
-  }
+  for (int i = threadIdx.x; i < nv; i += blockDim.x) out[i] = f4_e4m3(row[i], s);
   if (threadIdx.x == 0) scales[r] = s;
 }
 
 // One block per token: out[t] = bf16(sum_j fl32(w[t,j] * y2[row(t,j)])), the
-// float32 sum taken in slot order.  H % 4 == 0.
+// float32 sum taken in slot order.  H % 4 == 0.  The block walks its k rows
+// from start to end, so each row is read as one sequential stream.  KC > 0: top-k known at
+// compile time, so the k row loads of a column group are issued together
+// (one load in flight per thread would leave the kernel latency-bound).
+template <int KC>
 __global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ y2,
                                                   const float* __restrict__ weights,
                                                   const int32_t* __restrict__ slot_row,
-                                                  int32_t k, int32_t H,
+                                                  int32_t k_rt, int32_t H,
                                                   uint16_t* __restrict__ out) {
   const int64_t t = blockIdx.x;
+  const int k = KC > 0 ? KC : k_rt;
   const int nv = H / 4;
-  for (int i = blockIdx.y * blockDim.x + threadIdx.x; i < nv; i += gridDim.y * blockDim.x) {
+  for (int i = threadIdx.x; i < nv; i += blockDim.x) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const float w = weights[t * k + j];
-      const float4 y = reinterpret_cast<const float4*>(y2 + (int64_t)slot_row[t * k + j] * H)[i];
-      acc.x = __fadd_rn(acc.x, __fmul_rn(w, y.x));
-      acc.y = __fadd_rn(acc.y, __fmul_rn(w, y.y));
-      acc.z = __fadd_rn(acc.z, __fmul_rn(w, y.z));
-      acc.w = __fadd_rn(acc.w, __fmul_rn(w, y.w));
+    if constexpr (KC > 0) {
+      float4 y[KC];
+#pragma unroll
+      for (int j = 0; j < KC; ++j)
+        y[j] = reinterpret_cast<const float4*>(y2 + (int64_t)slot_row[t * KC + j] * H)[i];
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const float w = weights[t * KC + j];
+        acc.x = __fadd_rn(acc.x, __fmul_rn(w, y[j].x));
+        acc.y = __fadd_rn(acc.y, __fmul_rn(w, y[j].y));
+        acc.z = __fadd_rn(acc.z, __fmul_rn(w, y[j].z));
+        acc.w = __fadd_rn(acc.w, __fmul_rn(w, y[j].w));
+      }
+    } else {
+      for (int j = 0; j < k; ++j) {
+        const float w = weights[t * k + j];
+        const float4 y = reinterpret_cast<const float4*>(y2 + (int64_t)slot_row[t * k + j] * H)[i];
+        acc.x = __fadd_rn(acc.x, __fmul_rn(w, y.x));
+        acc.y = __fadd_rn(acc.y, __fmul_rn(w, y.y));
+        acc.z = __fadd_rn(acc.z, __fmul_rn(w, y.z));
+        acc.w = __fadd_rn(acc.w, __fmul_rn(w, y.w));
+      }
     }
     reinterpret_cast<uint2*>(out + t * H)[i] =
         make_uint2(bf16_bits(acc.x) | (bf16_bits(acc.y) << 16),
@@ -141,9 +205,15 @@ hipError_t launch_requant(const float* h, int64_t rows, int32_t I, int afmt_bf16
 hipError_t launch_finalize(const float* y2, const float* weights, const int32_t* slot_row,
                            int64_t T, int32_t k, int32_t H, uint16_t* out, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  // one block per (token, 1024 columns)
-  dim3 grid((unsigned)T, (unsigned)((H / 4 + 255) / 256));
-  k_finalize<<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out);
+  // one block per token, walking its k rows from start to end
+  const dim3 grid((unsigned)T);
+  switch (k) {
+    case 2: k_finalize<2><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
+    case 4: k_finalize<4><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
+    case 6: k_finalize<6><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
+    case 8: k_finalize<8><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
+    default: k_finalize<0><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
+  }
   return hipGetLastError();
 }
 

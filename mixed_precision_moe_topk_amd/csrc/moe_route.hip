@@ -125,11 +125,19 @@ __global__ __launch_bounds__(1024) void k_route_scan(RouteParams p) {
   const int e = threadIdx.x;  // blockDim.x == 1024 >= E
   int32_t run = 0;
   if (e < E) {
-    for (int c = 0; c < p.nchunks; ++c) {
-      const int64_t idx = (int64_t)c * E + e;
-      const int32_t v = p.chunk_counts[idx];
-      p.chunk_counts[idx] = run;  // rows of this expert in earlier chunks
-      run += v;
+    // exclusive prefix over chunks, 16 independent loads at a time (a chain
+    // of dependent loads would cost one memory latency per chunk)
+    constexpr int kB = 16;
+    for (int c0 = 0; c0 < p.nchunks; c0 += kB) {
+      int32_t v[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        v[u] = c0 + u < p.nchunks ? p.chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        if (c0 + u < p.nchunks) p.chunk_counts[(int64_t)(c0 + u) * E + e] = run;  // rows in earlier chunks
+        run += v[u];
+      }
     }
   }
   const int32_t nt = (run + p.tile_m - 1) / p.tile_m;
