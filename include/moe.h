@@ -163,14 +163,17 @@ moe_status moe_run(const moe_dims* dims, const void* hidden, int64_t num_tokens,
                    const float* router_logits, const void* weights, const void* scales,
                    int32_t top_k, void* out, hipStream_t stream);
 
-/* Stage timing.  While enabled, every moe_run_ws / moe_run call records a HIP
- * event on its stream before its first kernel and after each stage below
- * (events are created once and reused; recording adds no synchronisation).
- * moe_trace_read waits for the recorded events, writes the summed duration in
- * milliseconds of each stage over all recorded calls into stage_ms[0 ..
- * nstages) and the number of calls into *calls, then forgets them.  At most
- * 4096 calls are kept; later calls are not recorded.  Not for use under HIP
- * graph capture. */
+/* Stage timing.  With mode MOE_TRACE_ALL every moe_run_ws / moe_run call
+ * records a HIP event on its stream before its first kernel and after each
+ * stage below; with MOE_TRACE_GEMM1 only the two events around GEMM1 (each
+ * event costs a few microseconds of stream time, which matters for a
+ * decode-sized call of about a millisecond).  Events are created once and
+ * reused; recording adds no synchronisation.  moe_trace_read waits for the
+ * recorded events, writes the summed duration in milliseconds of each stage
+ * over all recorded calls into stage_ms[0 .. nstages) (stages a call did not
+ * time count as 0) and the number of calls into *calls, then forgets them.
+ * At most 4096 calls are kept; later calls are not recorded.  An unknown
+ * mode returns MOE_ERR_INVALID_ARG.  Not for use under HIP graph capture. */
 typedef enum {
   MOE_STAGE_ROUTE = 0,    /* router, routing index, work map */
   MOE_STAGE_QUANT = 1,    /* per-token E4M3 quantisation (FP8 activations) */
@@ -181,7 +184,8 @@ typedef enum {
   MOE_NUM_STAGES = 6
 } moe_stage;
 
-moe_status moe_trace_enable(int32_t on);
+enum { MOE_TRACE_OFF = 0, MOE_TRACE_ALL = 1, MOE_TRACE_GEMM1 = 2 };
+moe_status moe_trace_enable(int32_t mode);
 moe_status moe_trace_read(float* stage_ms, int32_t nstages, int32_t* calls);
 
 #ifdef __cplusplus

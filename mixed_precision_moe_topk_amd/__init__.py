@@ -163,8 +163,17 @@ def run(d: LayerDims, hidden, logits, weights, scales, top_k: int, out, stream=N
                          _ptr(scales), top_k, _ptr(out), _stream(stream)))
 
 
-def trace_enable(on: bool = True):
-    _check(lib().moe_trace_enable(1 if on else 0))
+TRACE_OFF, TRACE_ALL, TRACE_GEMM1 = 0, 1, 2
+
+
+def trace_enable(mode=TRACE_ALL):
+    """Stage timing: TRACE_ALL (every stage), TRACE_GEMM1 (GEMM1 only, two
+    events per call) or TRACE_OFF; True / False mean TRACE_ALL / TRACE_OFF."""
+    if mode is True:
+        mode = TRACE_ALL
+    elif mode is False:
+        mode = TRACE_OFF
+    _check(lib().moe_trace_enable(int(mode)))
 
 
 def trace_read():

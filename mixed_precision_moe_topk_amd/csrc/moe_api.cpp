@@ -194,11 +194,12 @@ moe_status check_device() {
 // ------------------------------------------------------------------ tracing
 struct TraceCall {
   hipEvent_t ev[MOE_NUM_STAGES + 1];
+  int32_t mode;  // MOE_TRACE_ALL or MOE_TRACE_GEMM1 when recorded
 };
 
 struct Tracer {
   std::mutex mu;
-  bool on = false;
+  int32_t mode = MOE_TRACE_OFF;
   std::vector<TraceCall> pool;  // events, reused across read cycles
   size_t used = 0;
   static constexpr size_t kMax = 4096;
@@ -206,7 +207,7 @@ struct Tracer {
   // Returns the event set of a new call, or null when tracing is off/full.
   TraceCall* next() {
     std::lock_guard<std::mutex> lk(mu);
-    if (!on || used >= kMax) return nullptr;
+    if (mode == MOE_TRACE_OFF || used >= kMax) return nullptr;
     if (used == pool.size()) {
       TraceCall c;
       for (auto& e : c.ev) {
@@ -214,6 +215,7 @@ struct Tracer {
       }
       pool.push_back(c);
     }
+    pool[used].mode = mode;
     return &pool[used++];
   }
 };
@@ -223,18 +225,23 @@ Tracer& tracer() {
   return t;
 }
 
+// Event i marks the end of stage i - 1 and the start of stage i.
 void trace_mark(TraceCall* tc, int i, hipStream_t st) {
-  if (tc) (void)hipEventRecord(tc->ev[i], st);
+  if (!tc) return;
+  if (tc->mode == MOE_TRACE_ALL || i == MOE_STAGE_GEMM1 || i == MOE_STAGE_GEMM1 + 1)
+    (void)hipEventRecord(tc->ev[i], st);
 }
 
 }  // namespace
 
 extern "C" {
 
-moe_status moe_trace_enable(int32_t on) {
+moe_status moe_trace_enable(int32_t mode) {
+  if (mode != MOE_TRACE_OFF && mode != MOE_TRACE_ALL && mode != MOE_TRACE_GEMM1)
+    return fail(MOE_ERR_INVALID_ARG, "trace mode %d", mode);
   Tracer& t = tracer();
   std::lock_guard<std::mutex> lk(t.mu);
-  t.on = on != 0;
+  t.mode = mode;
   return ok();
 }
 
@@ -245,9 +252,11 @@ moe_status moe_trace_read(float* stage_ms, int32_t nstages, int32_t* calls) {
   for (int i = 0; i < nstages; ++i) stage_ms[i] = 0.0f;
   for (size_t c = 0; c < t.used; ++c) {
     TraceCall& tc = t.pool[c];
-    hipError_t e = hipEventSynchronize(tc.ev[MOE_NUM_STAGES]);
+    const bool all = tc.mode == MOE_TRACE_ALL;
+    hipError_t e = hipEventSynchronize(tc.ev[all ? MOE_NUM_STAGES : MOE_STAGE_GEMM1 + 1]);
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
     for (int i = 0; i < nstages && i < MOE_NUM_STAGES; ++i) {
+      if (!all && i != MOE_STAGE_GEMM1) continue;
       float ms = 0.0f;
       e = hipEventElapsedTime(&ms, tc.ev[i], tc.ev[i + 1]);
       if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));

@@ -96,3 +96,11 @@ def test_workspace_layout_regions(L):
     assert lay.y2 + 4096 * 8 * 7168 * 4 <= lay.total
     assert lay.tile_m == 160 and lay.gemm_cfg == 2
     assert M.workspace_layout(_d(), 64, 8).tile_m == 16
+
+
+def test_trace_modes(L):
+    # off / all stages / GEMM1 only are accepted, anything else is an argument error
+    for mode in (M.TRACE_ALL, M.TRACE_GEMM1, M.TRACE_OFF):
+        assert L.moe_trace_enable(mode) == 0
+    assert L.moe_trace_enable(7) == 1
+    assert L.moe_trace_enable(M.TRACE_OFF) == 0

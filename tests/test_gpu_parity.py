@@ -61,6 +61,27 @@ def test_tiny_workload_all_stages():
     assert np.array_equal(g3["out"], g["out"])
 
 
+def test_trace_gemm1_only():
+    """GEMM1-only tracing times GEMM1 and leaves every other stage at zero;
+    full tracing times every stage."""
+    import mixed_precision_moe_topk_amd as M
+
+    wl = MI.WORKLOADS["tiny_mxfp4_fp8"]
+    p = Problem(wl, experts_for_oracle=[])
+    M.trace_read()  # forget anything recorded before
+    M.trace_enable(M.TRACE_GEMM1)
+    p.run_gpu()
+    M.trace_enable(M.TRACE_OFF)
+    calls, st = M.trace_read()
+    assert calls == 1 and st["gemm1"] > 0
+    assert all(v == 0 for k, v in st.items() if k != "gemm1")
+    M.trace_enable(M.TRACE_ALL)
+    p.run_gpu()
+    M.trace_enable(M.TRACE_OFF)
+    calls, st = M.trace_read()
+    assert calls == 1 and all(v > 0 for k, v in st.items() if k != "quant" or wl.afmt == "fp8")
+
+
 @pytest.mark.parametrize("E,k", [(8, 2), (64, 6), (256, 8), (384, 6), (1024, 16)])
 def test_router_ties_bit_exact(E, k):
     """Logits drawn from few values force exact ties at the top-k boundary;
