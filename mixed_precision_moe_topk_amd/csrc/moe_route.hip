@@ -18,11 +18,10 @@
 
 namespace moe {
 
-// One wave per token.  Lane j holds logits j, j+64, ... (E <= 1024).
-__global__ __launch_bounds__(256) void k_router(RouteParams p) {
+// Top-k and softmax of token t, by one wave.  Lane j holds logits j, j+64,
+// ... (E <= 1024).
+__device__ __forceinline__ void route_token(const RouteParams& p, const int64_t t) {
   const int lane = lane_id();
-  const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (t >= p.tokens) return;
   const int E = p.experts;
   const float* row = p.logits + t * E;
   constexpr int kPer = kMaxExperts / kWave;  // 16
@@ -89,6 +88,12 @@ __global__ __launch_bounds__(256) void k_router(RouteParams p) {
   }
 }
 
+// One wave per token.
+__global__ __launch_bounds__(256) void k_router(RouteParams p) {
+  const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (t < p.tokens) route_token(p, t);
+}
+
 // Routing index over chunks of kChunkTokens tokens (one wave per chunk).  For
 // every expert a 64-bit mask of the chunk's tokens that selected it is built
 // with atomic ORs in LDS (order-independent, so deterministic); the rank of
@@ -117,9 +122,46 @@ __global__ __launch_bounds__(64) void k_route_count(RouteParams p) {
 }
 
 // Single block: per-expert totals, chunk bases, expert offsets, tile list.
+// Thread e (blockDim.x == 1024 >= E) holds `run`, the rows of expert e.
+// Block-wide exclusive scans of the rows and of the tiles per expert (wave
+// scans + wave totals) give the expert offsets and the work map; returns the
+// first row of expert e.
+__device__ int32_t scan_experts(const RouteParams& p, const int32_t run, int32_t (*wsum)[16]) {
+  const int E = p.experts;
+  const int e = threadIdx.x;
+  const int32_t nt = (run + p.tile_m - 1) / p.tile_m;
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  int32_t a = run, b = nt;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t ya = __shfl_up(a, o), yb = __shfl_up(b, o);
+    if (lane >= o) { a += ya; b += yb; }
+  }
+  if (lane == kWave - 1) { wsum[0][w] = a; wsum[1][w] = b; }
+  __syncthreads();
+  int32_t pa = 0, pb = 0;
+  for (int i = 0; i < w; ++i) { pa += wsum[0][i]; pb += wsum[1][i]; }
+  const int32_t ex_a = pa + a - run, ex_b = pb + b - nt;
+  if (e == E - 1) {
+    p.offsets[E] = ex_a + run;
+    *p.num_tiles = ex_b + nt;
+  }
+  if (e < E) {
+    p.offsets[e] = ex_a;
+    int32_t ti = ex_b;
+    for (int32_t r = 0; r < run; r += p.tile_m, ++ti) {
+      Tile tl;
+      tl.expert = e;
+      tl.row0 = ex_a + r;
+      tl.nrows = min(p.tile_m, run - r);
+      tl.pad = 0;
+      p.tiles[ti] = tl;
+    }
+  }
+  return ex_a;
+}
+
 __global__ __launch_bounds__(1024) void k_route_scan(RouteParams p) {
-  __shared__ int32_t tot[kMaxExperts];
-  __shared__ int32_t ntl[kMaxExperts];
   __shared__ int32_t wsum[2][16];
   const int E = p.experts;
   const int e = threadIdx.x;  // blockDim.x == 1024 >= E
@@ -140,42 +182,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(RouteParams p) {
       }
     }
   }
-  const int32_t nt = (run + p.tile_m - 1) / p.tile_m;
-  // block-wide exclusive scans of run and nt (wave scans + wave totals)
-  const int lane = lane_id(), w = threadIdx.x / kWave;
-  int32_t a = run, b = nt;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int32_t ya = __shfl_up(a, o), yb = __shfl_up(b, o);
-    if (lane >= o) { a += ya; b += yb; }
-  }
-  if (lane == kWave - 1) { wsum[0][w] = a; wsum[1][w] = b; }
-  __syncthreads();
-  int32_t pa = 0, pb = 0;
-  for (int i = 0; i < w; ++i) { pa += wsum[0][i]; pb += wsum[1][i]; }
-  const int32_t ex_a = pa + a - run, ex_b = pb + b - nt;
-  if (e < E) {
-    p.offsets[e] = ex_a;
-    tot[e] = ex_a;
-    ntl[e] = ex_b;
-  }
-  if (e == E - 1) {
-    p.offsets[E] = ex_a + run;
-    *p.num_tiles = ex_b + nt;
-  }
-  __syncthreads();
-  if (e < E) {
-    const int32_t start = tot[e];
-    int32_t ti = ntl[e];
-    for (int32_t r = 0; r < run; r += p.tile_m, ++ti) {
-      Tile tl;
-      tl.expert = e;
-      tl.row0 = start + r;
-      tl.nrows = min(p.tile_m, run - r);
-      tl.pad = 0;
-      p.tiles[ti] = tl;
-    }
-  }
+  scan_experts(p, run, wsum);
 }
 
 __global__ __launch_bounds__(64) void k_route_scatter(RouteParams p) {
@@ -196,10 +203,46 @@ __global__ __launch_bounds__(64) void k_route_scatter(RouteParams p) {
   }
 }
 
+// Routing index of a batch of at most one chunk (64 tokens) in one block of
+// 1024 threads: the same masks, scan and ranks as the chunked kernels (so the
+// same results) in one launch instead of three.
+__global__ __launch_bounds__(1024) void k_route_small(RouteParams p) {
+  __shared__ uint64_t mask[kMaxExperts];
+  __shared__ int32_t offs[kMaxExperts];
+  __shared__ int32_t wsum[2][16];
+  const int E = p.experts, K = p.top_k;
+  const int tid = threadIdx.x;
+  if (tid < E) mask[tid] = 0;
+  __syncthreads();
+  if (tid < p.tokens) {
+    for (int j = 0; j < K; ++j)
+      atomicOr(reinterpret_cast<unsigned long long*>(&mask[p.ids[tid * K + j]]), 1ull << tid);
+  }
+  __syncthreads();
+  const int32_t run = tid < E ? __popcll(mask[tid]) : 0;
+  const int32_t first = scan_experts(p, run, wsum);
+  if (tid < E) offs[tid] = first;
+  __syncthreads();
+  if (tid < p.tokens) {
+    const uint64_t below = (1ull << tid) - 1ull;
+    for (int j = 0; j < K; ++j) {
+      const int64_t f = (int64_t)tid * K + j;
+      const int e = p.ids[f];
+      const int pos = offs[e] + __popcll(mask[e] & below);
+      p.row_token[pos] = tid;
+      p.slot_row[f] = pos;
+    }
+  }
+}
+
 hipError_t launch_route(const RouteParams& p, hipStream_t st) {
   if (p.tokens == 0) return hipSuccess;
   const int wpb = 4;
   k_router<<<(unsigned)((p.tokens + wpb - 1) / wpb), wpb * kWave, 0, st>>>(p);
+  if (p.tokens <= kChunkTokens) {
+    k_route_small<<<1, 1024, 0, st>>>(p);
+    return hipGetLastError();
+  }
   k_route_count<<<p.nchunks, 64, 0, st>>>(p);
   k_route_scan<<<1, 1024, 0, st>>>(p);
   k_route_scatter<<<p.nchunks, 64, 0, st>>>(p);
