@@ -43,7 +43,7 @@ class Workload:
     hidden: int
     inter: int
     wfmt: str  # "mxfp4" or "int4"
-    afmt: str  # "fp8" or "bf16"
+    afmt: str  # "fp8" (per-token E4M3), "mxfp8" (E4M3 + E8M0 per 32) or "bf16"
     bias_sigma: float = 0.0
     regime: str = ""
 
@@ -65,6 +65,9 @@ WORKLOADS = {
                                           2.0, "mfma"),
     "dsv3_int4_fp8": Workload("dsv3_int4_fp8", 5, 1024, 256, 8, 7168, 2048,
                               "int4", "fp8", 0.0, "hbm"),
+    # the DeepSeek-V3 prefill shape with MXFP8 activations (E8M0 per 32)
+    "dsv3_prefill_mxfp4_mxfp8": Workload("dsv3_prefill_mxfp4_mxfp8", 6, 4096, 256, 8,
+                                         7168, 2048, "mxfp4", "mxfp8", 0.0, "mfma"),
 }
 
 

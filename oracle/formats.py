@@ -49,6 +49,7 @@ def _e4m3_decode_scalar(code: int) -> float:
 
 E4M3_TABLE = np.array([_e4m3_decode_scalar(c) for c in range(256)], dtype=np.float64)
 E4M3_MAX = 448.0
+E4M3_EMAX = 8  # largest power of two in E4M3 (448 = 1.75 * 2^8); the MX element emax
 # Non-negative finite codes 0x00..0x7E; their values increase with the code.
 _E4M3_POS = E4M3_TABLE[:0x7F].copy()
 assert np.all(np.diff(_E4M3_POS) > 0)

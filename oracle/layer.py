@@ -15,13 +15,15 @@ and fuses the router-weighted reduction into a finalize step after GEMM2.
 Steps, each rounded only at its storage point:
   route     top-k by float32 logit (ties -> lower expert index), weights =
             softmax over the k selected logits (float64 exp), stored float32.
-  quantize  per-token E4M3 (FP8 activations) or the bf16 values (BF16).
+  quantize  per-token E4M3 (FP8 activations), MXFP8 (E4M3 with one E8M0
+            scale per 32 elements of a token; the token scale is then 1) or
+            the bf16 values (BF16).
   expand    rows grouped by expert, then token, then slot.
   gemm1     acc = A . W1^T exactly in float64; y1 = fl32(acc * token scale).
   swiglu    h = fl32(silu(gate) * up), gate = y1[:, :I], up = y1[:, I:],
             silu(g) = g / (1 + exp(-g)).
   fc2 input FP8: per-row E4M3 of h (same quantiser as the tokens);
-            BF16: bf16(h) with scale 1.
+            MXFP8: per-row MXFP8 of h (row scale 1); BF16: bf16(h), scale 1.
   gemm2     acc2 = A2 . W2^T in float64; y2 = fl32(acc2 * row scale).
   finalize  out[t] = bf16(sum_j fl32(w[t,j] * y2[row(t,j)])), the sum kept
             in float32 and taken in slot order.
@@ -117,9 +119,14 @@ def forward(hidden_bits: np.ndarray, logits: np.ndarray, top_k: int,
     e_num = logits.shape[1]
     ids, w = route(logits, top_k)
     x = F.bf16_to_f32(hidden_bits)
+    sx_tok = None
     if afmt == "fp8":
         q, s_tok = Q.e4m3_rows(x)
         a_dec = F.e4m3_decode(q)
+    elif afmt == "mxfp8":
+        q, sx_tok = Q.mxfp8_rows(x)
+        s_tok = np.ones(t, dtype=np.float32)
+        a_dec = Q.mxfp8_decode(q, sx_tok)
     elif afmt == "bf16":
         q, s_tok = None, np.ones(t, dtype=np.float32)
         a_dec = x.astype(np.float64)
@@ -128,7 +135,7 @@ def forward(hidden_bits: np.ndarray, logits: np.ndarray, top_k: int,
     offsets, row_tok, row_slot, slot_row = expand(ids, e_num)
     rows = t * top_k
     inter = None
-    h_all = y2 = q2 = s2 = y1_all = None
+    h_all = y2 = q2 = s2 = sx2 = y1_all = None
     for e in range(e_num):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         if r1 == r0:
@@ -140,12 +147,16 @@ def forward(hidden_bits: np.ndarray, logits: np.ndarray, top_k: int,
             inter = w1.shape[0] // 2
             h_all = np.zeros((rows, inter), dtype=np.float32)
             y2 = np.zeros((rows, h), dtype=np.float32)
-            q2 = np.zeros((rows, inter), dtype=np.uint8 if afmt == "fp8" else np.uint16)
+            q2 = np.zeros((rows, inter), dtype=np.uint16 if afmt == "bf16" else np.uint8)
             s2 = np.ones(rows, dtype=np.float32)
+            if afmt == "mxfp8":
+                sx2 = np.full((rows, inter // Q.MX_BLOCK), 127, dtype=np.uint8)
             if keep_y1:
                 y1_all = np.zeros((rows, 2 * inter), dtype=np.float32)
         if check_exact and wfmt == "mxfp4" and afmt == "fp8":
             assert Q.mx_exponent_spread(wts.w1s) <= 18 and Q.mx_exponent_spread(wts.w2s) <= 18
+        if check_exact and wfmt == "mxfp4" and afmt == "mxfp8":
+            assert Q.mx_exponent_spread(wts.w1s) + Q.mx_exponent_spread(sx_tok[toks]) <= 18
         acc = a_dec[toks] @ w1.T
         y1 = (acc * s_tok[toks][:, None].astype(np.float64)).astype(np.float32)
         if keep_y1:
@@ -155,6 +166,13 @@ def forward(hidden_bits: np.ndarray, logits: np.ndarray, top_k: int,
         if afmt == "fp8":
             qq, ss = Q.e4m3_rows(hh)
             a2 = F.e4m3_decode(qq)
+        elif afmt == "mxfp8":
+            qq, sxx = Q.mxfp8_rows(hh)
+            ss = np.ones(r1 - r0, dtype=np.float32)
+            a2 = Q.mxfp8_decode(qq, sxx)
+            sx2[r0:r1] = sxx
+            if check_exact and wfmt == "mxfp4":
+                assert Q.mx_exponent_spread(wts.w2s) + Q.mx_exponent_spread(sxx) <= 18
         else:
             qq = F.bf16_rne(hh)
             ss = np.ones(r1 - r0, dtype=np.float32)
@@ -170,6 +188,7 @@ def forward(hidden_bits: np.ndarray, logits: np.ndarray, top_k: int,
         acc_out = (acc_out + term).astype(np.float32)
     out = F.bf16_rne(acc_out)
     return dict(ids=ids, weights=w, token_codes=q, token_scales=s_tok,
-                offsets=offsets, row_token=row_tok, row_slot=row_slot,
-                slot_row=slot_row, h=h_all, fc2_codes=q2, fc2_scales=s2, y2=y2,
-                out_f32=acc_out, out=out, y1=y1_all)
+                token_block_scales=sx_tok, offsets=offsets, row_token=row_tok,
+                row_slot=row_slot, slot_row=slot_row, h=h_all, fc2_codes=q2,
+                fc2_scales=s2, fc2_block_scales=sx2, y2=y2, out_f32=acc_out,
+                out=out, y1=y1_all)

@@ -17,6 +17,13 @@ TEST INFRASTRUCTURE ONLY: nothing on the GPU path may import this module.
 * Per-token E4M3 activations (same page, Implementation Notes: per-token
   activation scales computed while expanding routed rows): s = amax/448 in
   float32, q = E4M3(x/s) with float32 division; an all-zero token gets s = 1.
+* MXFP8 activations (the MXFP8 inputs of PR #4793, "Unify MoE CuTe DSL
+  dispatch to be dtype agnostic", and of PR #3614's MXFP8xMXFP8 profiling):
+  E4M3 elements with one E8M0 scale per 32 consecutive elements of a row, by
+  the same OCP MX v1.0 conversion as the weights with the E4M3 element's
+  emax = 8: X = floor(log2(max|v|)) - 8 (clamped to [-127, 127]), elements
+  E4M3(v / 2^X) rounded to nearest-even and saturated at 448; an all-zero
+  block gets scale code 127.
 """
 from __future__ import annotations
 
@@ -142,6 +149,36 @@ def e4m3_rows(x: np.ndarray):
 
     _rows_parallel(x.shape[0], rows)
     return codes, s_all
+
+
+def mxfp8_rows(x: np.ndarray):
+    """Row-wise MXFP8: x float32 [R, C] (C % 32 == 0) -> (E4M3 codes uint8
+    [R, C], E8M0 scale codes uint8 [R, C/32])."""
+    x = np.asarray(x, dtype=np.float32)
+    r, c = x.shape
+    assert c % MX_BLOCK == 0
+    codes = np.empty((r, c), dtype=np.uint8)
+    scale_code = np.empty((r, c // MX_BLOCK), dtype=np.uint8)
+
+    def rows(sl):
+        blk = x[sl].reshape(-1, c // MX_BLOCK, MX_BLOCK).astype(np.float64)
+        amax = np.max(np.abs(blk), axis=-1)
+        nz = amax > 0
+        xe = np.where(nz, floor_log2(np.where(nz, amax, 1.0)) - F.E4M3_EMAX, 0)
+        xe = np.clip(xe, -127, 127)
+        scale_code[sl] = (xe + 127).astype(np.uint8)
+        v = np.ldexp(blk, -xe[..., None])  # exact power-of-two scaling in float64
+        codes[sl] = F.e4m3_encode(v).reshape(-1, c)
+
+    _rows_parallel(r, rows)
+    return codes, scale_code
+
+
+def mxfp8_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """E4M3 codes [R, C] + E8M0 [R, C/32] -> float64 [R, C] (exact)."""
+    r, c = codes.shape
+    el = F.e4m3_decode(codes).reshape(r, c // MX_BLOCK, MX_BLOCK)
+    return (el * F.e8m0_decode(scales)[..., None]).reshape(r, c)
 
 
 def mx_exponent_spread(scales: np.ndarray) -> int:

@@ -101,7 +101,8 @@ def test_expand_structure():
 
 # ----------------------------------------------------------------------------- exact GEMMs
 
-@pytest.mark.parametrize("wfmt,afmt", [("mxfp4", "fp8"), ("mxfp4", "bf16"), ("int4", "fp8")])
+@pytest.mark.parametrize("wfmt,afmt", [("mxfp4", "fp8"), ("mxfp4", "bf16"), ("int4", "fp8"),
+                                       ("mxfp4", "mxfp8")])
 def test_gemms_against_exact_rationals(wfmt, afmt):
     wl = MI.small_workload(tokens=3, experts=4, top_k=2, hidden=128, inter=128,
                            wfmt=wfmt, afmt=afmt, seed=77)
@@ -112,6 +113,11 @@ def test_gemms_against_exact_rationals(wfmt, afmt):
     x = F.bf16_to_f32(hb)
     if afmt == "fp8":
         a_dec = [[Fraction(float(v)) for v in F.e4m3_decode(row)] for row in r["token_codes"]]
+    elif afmt == "mxfp8":
+        # element times 2^(code - 127) of its 32-element block, as exact rationals
+        a_dec = [[Fraction(float(F.e4m3_decode(c))) * Fraction(2) ** (int(sc[i // 32]) - 127)
+                  for i, c in enumerate(row)]
+                 for row, sc in zip(r["token_codes"], r["token_block_scales"])]
     else:
         a_dec = [[Fraction(float(v)) for v in row] for row in x]
     off = r["offsets"]
@@ -137,6 +143,10 @@ def test_gemms_against_exact_rationals(wfmt, afmt):
                     assert abs(got - exp) <= abs(exp) * 2.0 ** -23, (row, n, got, exp)
             if afmt == "fp8":
                 a2 = [Fraction(float(v)) for v in F.e4m3_decode(r["fc2_codes"][row])]
+            elif afmt == "mxfp8":
+                sc2 = r["fc2_block_scales"][row]
+                a2 = [Fraction(float(F.e4m3_decode(c))) * Fraction(2) ** (int(sc2[i // 32]) - 127)
+                      for i, c in enumerate(r["fc2_codes"][row])]
             else:
                 a2 = [Fraction(float(v)) for v in F.bf16_to_f32(r["fc2_codes"][row])]
             s2 = Fraction(float(r["fc2_scales"][row]))
@@ -198,7 +208,22 @@ def test_hand_derived_single_expert():
     assert np.array_equal(r["out"][0], F.bf16_rne(exp_y))
 
 
-@pytest.mark.parametrize("wfmt,afmt", [("mxfp4", "fp8"), ("mxfp4", "bf16"), ("int4", "fp8")])
+def _torch_mxfp8(x):
+    """MXFP8 of float32 rows with torch ops: per 32-element block X from the
+    exact binary exponent of the block's amax (torch.frexp), E4M3 codes of
+    x / 2^X, returned decoded (float64)."""
+    r, c = x.shape
+    b = x.reshape(r, c // 32, 32).double()
+    amax = b.abs().amax(dim=-1)
+    _, e = torch.frexp(torch.where(amax > 0, amax, torch.ones_like(amax)))
+    xe = torch.where(amax > 0, e.double() - 1 - 8, torch.zeros_like(amax)).clamp(-127, 127)
+    v = (b / torch.pow(2.0, xe)[..., None]).numpy()
+    dec = torch.from_numpy(F.e4m3_decode(F.e4m3_encode(v)))
+    return (dec * torch.pow(2.0, xe)[..., None]).reshape(r, c)
+
+
+@pytest.mark.parametrize("wfmt,afmt", [("mxfp4", "fp8"), ("mxfp4", "bf16"), ("int4", "fp8"),
+                                       ("mxfp4", "mxfp8")])
 def test_single_expert_equals_independent_mlp(wfmt, afmt):
     """E = 1, k = 1: out = bf16(MLP(x)) computed here with torch float64 ops on
     the decoded operands (an independent composition of the steps)."""
@@ -214,6 +239,9 @@ def test_single_expert_equals_independent_mlp(wfmt, afmt):
         amax = x.abs().amax(dim=1)
         s = amax / 448.0                             # float32 tensor division
         a = torch.from_numpy(F.e4m3_decode(F.e4m3_encode((x / s[:, None]).numpy())))
+    elif afmt == "mxfp8":
+        s = torch.ones(wl.tokens)
+        a = _torch_mxfp8(x)
     else:
         s = torch.ones(wl.tokens)
         a = x.double()
@@ -225,6 +253,9 @@ def test_single_expert_equals_independent_mlp(wfmt, afmt):
     if afmt == "fp8":
         s2 = hh.abs().amax(dim=1) / 448.0
         a2 = torch.from_numpy(F.e4m3_decode(F.e4m3_encode((hh / s2[:, None]).numpy())))
+    elif afmt == "mxfp8":
+        s2 = torch.ones(wl.tokens)
+        a2 = _torch_mxfp8(hh)
     else:
         s2 = torch.ones(wl.tokens)
         a2 = hh.to(torch.bfloat16).double()

@@ -1,5 +1,7 @@
 """Pins of the oracle's quantisers: a hand-worked MX block, brute-force scale
 search, invariants of MXFP4/INT4/E4M3 quantisation (CPU only)."""
+from fractions import Fraction
+
 import numpy as np
 
 from oracle import formats as F
@@ -119,3 +121,68 @@ def test_token_quant_power_of_two_invariance():
 def test_zero_token_gets_unit_scale():
     q, s = Q.e4m3_rows(np.zeros((2, 64), dtype=np.float32))
     assert np.all(s == 1.0) and np.all(q == 0)
+
+
+# ----------------------------------------------------------------------------- MXFP8
+
+def _brute_scale8(amax):
+    """Largest integer X (clamped to [-127, 127]) with 2^(X + 8) <= amax: the
+    OCP MX shared exponent for an E4M3 element (emax 8), found by search."""
+    for x in range(127, -128, -1):
+        if Fraction(2) ** (x + 8) <= Fraction(float(amax)):
+            return x
+    return -127
+
+
+def test_mxfp8_scale_and_elements_brute_force():
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((32, 256)) * np.exp(rng.uniform(-30, 30, (32, 1)))).astype(np.float32)
+    x[2, 64:96] = 0.0
+    x[3, 96:128] = -0.0
+    x[4, :32] = np.float32(2.0 ** -140)   # shared exponent below the E8M0 range -> -127
+    x[5, 32:64] = np.float32(448.0 * 2.0 ** 20)  # block amax exactly 448 * 2^20
+    q, s = Q.mxfp8_rows(x)
+    blk = x.reshape(32, 8, 32).astype(np.float64)
+    pos = F.E4M3_TABLE[:0x7F]
+    for r in range(32):
+        for b in range(8):
+            amax = np.max(np.abs(blk[r, b]))
+            if amax == 0:
+                assert s[r, b] == 127
+                exp_codes = np.signbit(blk[r, b]).astype(np.uint8) << 7
+            else:
+                xe = _brute_scale8(amax)
+                assert s[r, b] == xe + 127, (r, b)
+                v = blk[r, b] / 2.0 ** xe
+                mag = np.minimum(np.abs(v), 448.0)
+                d = np.abs(mag[:, None] - pos[None, :])
+                best = d.min(axis=1, keepdims=True)
+                # nearest, exact ties to the even code (mantissa lsb 0)
+                sc = np.where(d == best, 0, 10) + (np.arange(len(pos))[None, :] & 1)
+                exp_codes = np.argmin(sc, axis=1).astype(np.uint8) | (np.signbit(v).astype(np.uint8) << 7)
+            assert np.array_equal(q[r, b * 32:(b + 1) * 32], exp_codes), (r, b)
+    assert s[4, 0] == 0
+    assert s[5, 1] == 20 + 127 and np.all(q[5, 32:64] == 0x7E)
+
+
+def test_mxfp8_invariants():
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((64, 1024)).astype(np.float32)
+    q, s = Q.mxfp8_rows(x)
+    # amax * 2^-X lies in [256, 512): its code decodes to [256, 448]
+    bmax = np.abs(F.e4m3_decode(q)).reshape(64, 32, 32).max(axis=-1)
+    assert np.all((bmax >= 256) & (bmax <= 448))
+    d = Q.mxfp8_decode(q, s)
+    sc = F.e8m0_decode(s).repeat(32, axis=1)
+    err = np.abs(d - x)
+    # inside the grid the error is at most half a spacing (<= 2^-4 |x|, and
+    # <= 16 * 2^X at the top binade); [448, 512) * 2^X clamps to 448
+    inside = np.abs(x) <= 448 * sc
+    assert np.all(err[inside] <= np.maximum(np.abs(x[inside]) * 2.0 ** -4, 2.0 ** -10 * sc[inside]))
+    assert np.all(err <= 64 * sc)
+    # decode(encode(decoded)) is a fixed point
+    q2, s2 = Q.mxfp8_rows(d.astype(np.float32))
+    assert np.array_equal(q2, q) and np.array_equal(s2, s)
+    # scaling a row by 2^k shifts its scale codes by k and keeps its codes
+    q3, s3 = Q.mxfp8_rows((x * np.float32(2.0 ** 5)).astype(np.float32))
+    assert np.array_equal(q3, q) and np.array_equal(s3.astype(int), s.astype(int) + 5)
