@@ -35,12 +35,12 @@ sys.path.insert(0, ROOT)
 import moe_inputs as MI  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "mxfp8": 5000.0, "bf16": 2500.0}
 COPY_CALIB_BYTES = 256 << 20
 METRIC = "fused-MoE tokens/s + % MFMA peak (prefill) / % HBM GB/s (decode), 1 GPU"
 ORACLE_SAMPLE_TOKENS = {"tiny_mxfp4_fp8": 16, "dsv3_decode_mxfp4_bf16": 10,
                         "dsv3_prefill_mxfp4_fp8": 6, "dsv4pro_prefill_mxfp4_fp8": 6,
-                        "dsv3_int4_fp8": 6}
+                        "dsv3_int4_fp8": 6, "dsv3_prefill_mxfp4_mxfp8": 6}
 CSRC = "mixed_precision_moe_topk_amd/csrc/"
 
 
@@ -225,7 +225,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.afmt == "bf16" else "fp8",
+        "dtype": "bf16" if wl.afmt == "bf16" else "fp8",  # E4M3 operands (MXFP8 too)
         "data": "synthetic",
         "config": {"workload": wl.key, "tokens": wl.tokens, "experts": wl.experts,
                    "top_k": wl.top_k, "hidden": wl.hidden, "inter": wl.inter,

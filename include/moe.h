@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -61,7 +61,11 @@ typedef enum {
 } moe_status;
 
 typedef enum { MOE_W_MXFP4 = 0, MOE_W_INT4_G128 = 1 } moe_wfmt;
-typedef enum { MOE_A_FP8_TOKEN = 0, MOE_A_BF16 = 1 } moe_afmt;
+/* Activations: FP8_TOKEN = E4M3 with one float32 scale per token (and per FC2
+ * input row); MXFP8 = E4M3 with one E8M0 scale per 32 consecutive elements of
+ * a token (and of an FC2 input row), applied inside the block-scaled MFMA
+ * (MXFP4 weights only); BF16 = the activations as given. */
+typedef enum { MOE_A_FP8_TOKEN = 0, MOE_A_BF16 = 1, MOE_A_MXFP8 = 2 } moe_afmt;
 
 /* Shape and formats of one MoE layer.  W1 is [2*inter, hidden] per expert
  * (rows [0, inter) gate, [inter, 2*inter) up); W2 is [hidden, inter]. */
@@ -81,11 +85,16 @@ typedef struct {
  *   row_token   int32  [T*k]    token of each expanded row (expert-major,
  *                               then token, then slot)
  *   slot_row    int32  [T, k]   expanded row of each (token, slot)
- *   tok_codes   uint8  [T, H]   E4M3 token codes (FP8 activations only)
+ *   tok_codes   uint8  [T, H]   E4M3 token codes (FP8 and MXFP8 activations)
  *   tok_scales  float  [T]      token scales (FP8 activations only)
  *   h           float  [T*k, I] SwiGLU output per expanded row
- *   fc2_codes   uint8  [T*k, I] E4M3 (FP8) or bf16 bits ([T*k, I] uint16)
- *   fc2_scales  float  [T*k]    per-row FC2 input scale (1.0 for BF16)
+ *   fc2_codes   uint8  [T*k, I] E4M3 (FP8, MXFP8) or bf16 bits ([T*k, I] uint16)
+ *   fc2_scales  float  [T*k]    per-row FC2 input scale (1.0 for BF16 and MXFP8)
+ *   tok_bscales uint8  [T, 16*ceil(H/512)]   E8M0 block scales of the token
+ *                                  codes (MXFP8 only), in matrix-core order:
+ *                                  the scale of elements [32b, 32b + 32) of a
+ *                                  row sits at byte 16*(b/16) + 4*(b%4) + (b/4)%4
+ *   fc2_bscales uint8  [T*k, 16*ceil(I/512)] same for the FC2 codes (MXFP8 only)
  *   y2          float  [T*k, H] GEMM2 output per expanded row
  *   num_tiles   int32  [1]      GEMM work-map length; tile_m rows per tile */
 typedef struct {
@@ -95,6 +104,7 @@ typedef struct {
   int32_t tile_m;
   int32_t gemm_cfg;
   int64_t max_tiles;
+  size_t tok_bscales, fc2_bscales;
 } moe_ws_layout;
 
 int32_t moe_abi_version(void);

@@ -15,9 +15,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_amd.so")
 
 W_MXFP4, W_INT4_G128 = 0, 1
-A_FP8_TOKEN, A_BF16 = 0, 1
+A_FP8_TOKEN, A_BF16, A_MXFP8 = 0, 1, 2
 WFMT = {"mxfp4": W_MXFP4, "int4": W_INT4_G128}
-AFMT = {"fp8": A_FP8_TOKEN, "bf16": A_BF16}
+AFMT = {"fp8": A_FP8_TOKEN, "bf16": A_BF16, "mxfp8": A_MXFP8}
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP", 5: "MOE_ERR_INTERNAL"}
@@ -43,7 +43,8 @@ class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "total", "ids", "topk_w", "chunk_counts", "offsets", "row_token", "slot_row", "tiles",
         "num_tiles", "tok_codes", "tok_scales", "h", "fc2_codes", "fc2_scales", "y2")] + [
-        ("tile_m", ctypes.c_int32), ("gemm_cfg", ctypes.c_int32), ("max_tiles", ctypes.c_int64)]
+        ("tile_m", ctypes.c_int32), ("gemm_cfg", ctypes.c_int32), ("max_tiles", ctypes.c_int64),
+        ("tok_bscales", ctypes.c_size_t), ("fc2_bscales", ctypes.c_size_t)]
 
 
 _lib = None

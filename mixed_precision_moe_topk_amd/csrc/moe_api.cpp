@@ -83,10 +83,10 @@ moe_status check_dims(const moe_dims* d) {
     return fail(MOE_ERR_INVALID_ARG, "inter %d must be a positive multiple of 128", d->inter);
   if (d->wfmt != MOE_W_MXFP4 && d->wfmt != MOE_W_INT4_G128)
     return fail(MOE_ERR_INVALID_ARG, "unknown weight format %d", d->wfmt);
-  if (d->afmt != MOE_A_FP8_TOKEN && d->afmt != MOE_A_BF16)
+  if (d->afmt != MOE_A_FP8_TOKEN && d->afmt != MOE_A_BF16 && d->afmt != MOE_A_MXFP8)
     return fail(MOE_ERR_INVALID_ARG, "unknown activation format %d", d->afmt);
-  if (d->wfmt == MOE_W_INT4_G128 && d->afmt == MOE_A_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "INT4 weights with BF16 activations are not supported");
+  if (d->wfmt == MOE_W_INT4_G128 && d->afmt != MOE_A_FP8_TOKEN)
+    return fail(MOE_ERR_UNSUPPORTED, "INT4 weights take per-token FP8 activations only");
   return MOE_OK;
 }
 
@@ -114,6 +114,7 @@ Sizes sizes_of(const moe_dims* d) {
 
 int variant_of(const moe_dims* d) {
   if (d->wfmt == MOE_W_INT4_G128) return moe::kInt4Fp8;
+  if (d->afmt == MOE_A_MXFP8) return moe::kMxfp4Mxfp8;
   return d->afmt == MOE_A_BF16 ? moe::kMxfp4Bf16 : moe::kMxfp4Fp8;
 }
 
@@ -156,13 +157,15 @@ moe_status layout_of(const moe_dims* d, int64_t T, int32_t k, moe_ws_layout* L) 
   L->slot_row = take(rows * 4);
   L->tiles = take(max_tiles * sizeof(moe::Tile));
   L->num_tiles = take(4);
-  const bool fp8 = d->afmt == MOE_A_FP8_TOKEN;
-  L->tok_codes = take(fp8 ? T * H : 0);
-  L->tok_scales = take(fp8 ? T * 4 : 0);
+  const bool e4m3 = d->afmt != MOE_A_BF16, mx = d->afmt == MOE_A_MXFP8;
+  L->tok_codes = take(e4m3 ? T * H : 0);
+  L->tok_scales = take(e4m3 ? T * 4 : 0);
   L->h = take(rows * I * 4);
-  L->fc2_codes = take(rows * I * (fp8 ? 1 : 2));
+  L->fc2_codes = take(rows * I * (e4m3 ? 1 : 2));
   L->fc2_scales = take(rows * 4);
   L->y2 = take(rows * H * 4);
+  L->tok_bscales = take(mx ? T * moe::mx_scale_row_bytes(H) : 0);
+  L->fc2_bscales = take(mx ? rows * moe::mx_scale_row_bytes(I) : 0);
   L->total = off;
   L->tile_m = tile_m;
   L->gemm_cfg = cfg;
@@ -381,7 +384,7 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
   const Sizes s = sizes_of(dims);
   const int64_t T = num_tokens, rows = T * top_k;
   const int32_t E = dims->num_experts, H = dims->hidden, I = dims->inter;
-  const bool fp8 = dims->afmt == MOE_A_FP8_TOKEN;
+  const bool fp8 = dims->afmt == MOE_A_FP8_TOKEN, mx = dims->afmt == MOE_A_MXFP8;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
 
   moe::RouteParams rp;
@@ -403,14 +406,19 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
   trace_mark(tc, 1, stream);
 
   const float* tok_scales = nullptr;
+  const uint8_t* tok_bscales = nullptr;
   const uint8_t* a1 = static_cast<const uint8_t*>(hidden);
   int64_t a1_stride = (int64_t)H * 2;
-  if (fp8) {
+  if (fp8 || mx) {
     uint8_t* codes = ws + L.tok_codes;
     float* sc = reinterpret_cast<float*>(ws + L.tok_scales);
+    uint8_t* bsc = mx ? ws + L.tok_bscales : nullptr;
     MOE_TRY(hip_check(moe::launch_quant_tokens(static_cast<const uint16_t*>(hidden), T, H,
-                                               codes, sc, stream), "quantize tokens", stream));
-    tok_scales = sc;
+                                               mx ? moe::kQuantMxfp8 : moe::kQuantFp8Row,
+                                               codes, sc, bsc, stream),
+                      "quantize tokens", stream));
+    if (fp8) tok_scales = sc;
+    tok_bscales = bsc;
     a1 = codes;
     a1_stride = H;
   }
@@ -427,6 +435,8 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
   g1.a_stride = a1_stride;
   g1.row_token = rp.row_token;
   g1.row_scale = tok_scales;
+  g1.a_scale = tok_bscales;
+  g1.a_scale_stride = moe::mx_scale_row_bytes(H);
   g1.w = wbytes;
   g1.w_expert_stride = s.codes_per_expert;
   g1.s = sbytes;
@@ -444,16 +454,20 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
 
   uint8_t* q2 = ws + L.fc2_codes;
   float* s2 = reinterpret_cast<float*>(ws + L.fc2_scales);
-  MOE_TRY(hip_check(moe::launch_requant(h, rows, I, fp8 ? 0 : 1, q2, s2, stream),
+  uint8_t* b2 = mx ? ws + L.fc2_bscales : nullptr;
+  const int rq_mode = fp8 ? moe::kQuantFp8Row : (mx ? moe::kQuantMxfp8 : moe::kQuantBf16);
+  MOE_TRY(hip_check(moe::launch_requant(h, rows, I, rq_mode, q2, s2, b2, stream),
                     "fc2 requant", stream));
   trace_mark(tc, 4, stream);
 
   float* y2 = reinterpret_cast<float*>(ws + L.y2);
   moe::GemmParams g2;
   g2.a = q2;
-  g2.a_stride = (int64_t)I * (fp8 ? 1 : 2);
+  g2.a_stride = (int64_t)I * (fp8 || mx ? 1 : 2);
   g2.row_token = nullptr;
   g2.row_scale = fp8 ? s2 : nullptr;
+  g2.a_scale = b2;
+  g2.a_scale_stride = moe::mx_scale_row_bytes(I);
   g2.w = wbytes + s.w1_codes;
   g2.w_expert_stride = s.codes_per_expert;
   g2.s = sbytes + s.w1_scales;

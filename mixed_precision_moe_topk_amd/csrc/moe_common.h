@@ -20,7 +20,13 @@ enum Variant : int {
   kMxfp4Fp8 = 0,   // E2M1 weights (E8M0 / 32) x per-token E4M3 activations
   kMxfp4Bf16 = 1,  // E2M1 weights (E8M0 / 32) x bf16 activations
   kInt4Fp8 = 2,    // INT4 weights (fp32 / 128) x per-token E4M3 activations
+  kMxfp4Mxfp8 = 3, // E2M1 weights (E8M0 / 32) x E4M3 activations (E8M0 / 32)
 };
+
+// Weights and activations both carry E8M0 block scales, applied by the MFMA.
+constexpr bool a_blockscaled(int v) { return v == kMxfp4Mxfp8; }
+// E2M1 weights with E4M3 activations: the block-scaled FP8 x FP4 MFMA.
+constexpr bool fp8_x_fp4(int v) { return v == kMxfp4Fp8 || v == kMxfp4Mxfp8; }
 
 // Work-map entry of the grouped GEMMs: rows [row0, row0 + nrows) of expert
 // `expert` (entries are grouped by expert, in expert order).
@@ -129,7 +135,9 @@ struct GemmParams {
   const uint8_t* a;            // FC1: token rows (E4M3 or bf16); FC2: expanded rows
   int64_t a_stride;            // bytes per A row
   const int32_t* row_token;    // FC1 gather map (expanded row -> token); null for FC2
-  const float* row_scale;      // FC1: per-token scale; FC2: per-row scale; null for bf16
+  const float* row_scale;      // FC1: per-token scale; FC2: per-row scale; null for bf16 and MXFP8
+  const uint8_t* a_scale;      // MXFP8: E8M0 scales of A in MFMA scale order (FC1 rows gathered); else null
+  int64_t a_scale_stride;      // bytes per A row of a_scale (mx_scale_row_bytes(K))
   const uint8_t* w;            // packed weights of expert 0 of this matrix
   int64_t w_expert_stride;     // bytes between experts
   const uint8_t* s;            // scales of expert 0 of this matrix
@@ -143,12 +151,30 @@ struct GemmParams {
   int64_t out_stride;          // floats per output row
 };
 
+// E8M0 block scales of MXFP8 activations, stored in the order the block-scaled
+// MFMA takes them: per row, one 16-byte group per four 128-wide K steps; in a
+// group, the dword of k-block g (elements [32g, 32g + 32) of a step) holds
+// the scales of the four steps in bytes 0..3.  Lane l of an MFMA then loads
+// the dword of its row and of k-block l/16 once per four steps and selects
+// the step's byte with the MFMA's scale byte select, as for the weights.
+__host__ __device__ constexpr int64_t mx_scale_row_bytes(int64_t cols) {
+  return 16 * ((cols + 511) / 512);
+}
+__host__ __device__ constexpr int64_t mx_scale_offset(int64_t kb) {  // kb = col / 32
+  return 16 * (kb >> 4) + 4 * (kb & 3) + ((kb >> 2) & 3);
+}
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_route(const RouteParams& p, hipStream_t st);
-hipError_t launch_quant_tokens(const uint16_t* x, int64_t T, int32_t H, uint8_t* codes,
-                               float* scales, hipStream_t st);
-hipError_t launch_requant(const float* h, int64_t rows, int32_t I, int afmt_bf16,
-                          uint8_t* codes, float* scales, hipStream_t st);
+// Activation quantisation modes of the token and FC2-input quantisers.
+enum QuantMode : int { kQuantFp8Row = 0, kQuantBf16 = 1, kQuantMxfp8 = 2 };
+// FP8 rows: codes + one float scale per row; MXFP8: codes + E8M0 per 32
+// (bscales [rows][mx_scale_row_bytes(C)] in MFMA scale order, row scales
+// written as 1.0); BF16: bits, scale 1.
+hipError_t launch_quant_tokens(const uint16_t* x, int64_t T, int32_t H, int mode,
+                               uint8_t* codes, float* scales, uint8_t* bscales, hipStream_t st);
+hipError_t launch_requant(const float* h, int64_t rows, int32_t I, int mode, uint8_t* codes,
+                          float* scales, uint8_t* bscales, hipStream_t st);
 hipError_t launch_finalize(const float* y2, const float* weights, const int32_t* slot_row,
                            int64_t T, int32_t k, int32_t H, uint16_t* out, hipStream_t st);
 hipError_t launch_gemm(int variant, bool fc1, int cfg, const GemmParams& p, int64_t max_tiles,
@@ -180,9 +206,10 @@ inline GemmCfg gemm_cfg(int i, int variant) {
     case 0: return GemmCfg{4, 1, 1, 2};                                        // 16 x 128
     case 1: return variant == kMxfp4Bf16 ? GemmCfg{4, 1, 3, 2} : GemmCfg{4, 1, 4, 4};  // 48 x 128 / 64 x 256
     default:
-      return variant == kMxfp4Bf16 ? GemmCfg{4, 2, 4, 4}     // 128 x 128
-             : variant == kMxfp4Fp8 ? GemmCfg{8, 2, 5, 8}   // 160 x 512
-                                    : GemmCfg{8, 2, 4, 4};  // 128 x 256
+      return variant == kMxfp4Bf16 ? GemmCfg{4, 2, 4, 4}    // 128 x 128
+             : variant == kMxfp4Mxfp8 ? GemmCfg{8, 2, 4, 8}  // 128 x 512
+             : variant == kMxfp4Fp8 ? GemmCfg{8, 2, 5, 8}    // 160 x 512
+                                  : GemmCfg{8, 2, 4, 4};   // 128 x 256
   }
 }
 

@@ -143,6 +143,80 @@ __global__ __launch_bounds__(256) void k_requant(const float* __restrict__ h, in
   if (threadIdx.x == 0) scales[r] = s;
 }
 
+// ---------------------------------------------------------------- MXFP8
+// OCP MX conversion with E4M3 elements (emax 8): per 32 consecutive elements
+// X = floor(log2 amax) - 8 (clamped to [-127, 127]; amax = 0 -> code 127),
+// elements E4M3(v * 2^-X) rounded to nearest even and saturated at 448.
+// v * 2^-X is exact in float32 unless the product is below 2^-126, where the
+// E4M3 code is +-0 either way.  (MXFP8 inputs of flashinfer PR #4793, "Unify
+// MoE CuTe DSL dispatch to be dtype agnostic", and PR #3614's MXFP8xMXFP8.)
+__device__ __forceinline__ int mx_e4m3_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const uint32_t b = __float_as_uint(amax);
+  const int e = (int)((b >> 23) & 0xFFu);
+  const int fl = e ? e - 127 : (31 - __clz(b & 0x7FFFFFu)) - 149;  // floor(log2 amax)
+  return min(max(fl - 8, -127), 127);
+}
+
+// Eight consecutive elements per thread, four threads (consecutive lanes) per
+// 32-element block.  `valid`: the group's block lies inside the row (rows are
+// a multiple of 32 long, so a group is wholly inside or outside).  Returns
+// the eight codes; *code = the block's E8M0 code.
+__device__ __forceinline__ uint2 mx_quant8(const float (&v)[8], bool valid, uint32_t* code) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  if (!valid) amax = 0.0f;
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const int x = mx_e4m3_exponent(amax);
+  *code = (uint32_t)(x + 127);
+  const float inv = __uint_as_float((uint32_t)(127 - x) << 23);  // 2^-X, a normal float
+  uint32_t c[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i / 4] |= e4m3_encode(v[i] * inv) << (8 * (i & 3));
+  return make_uint2(c[0], c[1]);
+}
+
+// One block (256 threads) per row of C elements (C % 32 == 0), 2048 elements
+// per pass: bf16 (SRC_BF16) or float32 input -> E4M3 codes [C] + E8M0 codes
+// in the block-scaled MFMA's scale order (mx_scale_offset); the row's float
+// scale is written as 1.0.
+template <bool SRC_BF16>
+__global__ __launch_bounds__(256) void k_quant_mx(const void* __restrict__ src, int32_t C,
+                                                  uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ bscales,
+                                                  float* __restrict__ scales) {
+  const int64_t r = blockIdx.x;
+  for (int i = threadIdx.x; 8 * (i - (int)(threadIdx.x & 3)) < C; i += 256) {
+    const bool valid = 8 * i < C;
+    float v[8];
+    if (SRC_BF16) {
+      const uint4 u = valid ? reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + r * C)[i]
+                            : make_uint4(0, 0, 0, 0);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __uint_as_float(w[j] << 16);
+        v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+    } else {
+      const float4* row = reinterpret_cast<const float4*>(static_cast<const float*>(src) + r * C);
+      const float4 a = valid ? row[2 * i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 b = valid ? row[2 * i + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    uint32_t code;
+    const uint2 q = mx_quant8(v, valid, &code);
+    if (valid) {
+      reinterpret_cast<uint2*>(codes + r * C)[i] = q;
+      if ((i & 3) == 0) bscales[r * mx_scale_row_bytes(C) + mx_scale_offset(i / 4)] = (uint8_t)code;
+    }
+  }
+  if (threadIdx.x == 0) scales[r] = 1.0f;
+}
+
 // One block per token: out[t] = bf16(sum_j fl32(w[t,j] * y2[row(t,j)])), the
 // float32 sum taken in slot order.  H % 4 == 0.  The block walks its k rows
 // from start to end, so each row is read as one sequential stream.  KC > 0: top-k known at
@@ -188,17 +262,21 @@ __global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ y2,
   }
 }
 
-hipError_t launch_quant_tokens(const uint16_t* x, int64_t T, int32_t H, uint8_t* codes,
-                               float* scales, hipStream_t st) {
+hipError_t launch_quant_tokens(const uint16_t* x, int64_t T, int32_t H, int mode,
+                               uint8_t* codes, float* scales, uint8_t* bscales, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  k_quant_tokens<<<(unsigned)T, 256, 0, st>>>(x, H, codes, scales);
+  if (mode == kQuantMxfp8) k_quant_mx<true><<<(unsigned)T, 256, 0, st>>>(x, H, codes, bscales, scales);
+  else k_quant_tokens<<<(unsigned)T, 256, 0, st>>>(x, H, codes, scales);
   return hipGetLastError();
 }
 
-hipError_t launch_requant(const float* h, int64_t rows, int32_t I, int afmt_bf16,
-                          uint8_t* codes, float* scales, hipStream_t st) {
+hipError_t launch_requant(const float* h, int64_t rows, int32_t I, int mode, uint8_t* codes,
+                          float* scales, uint8_t* bscales, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  k_requant<<<(unsigned)rows, 256, 0, st>>>(h, I, afmt_bf16, codes, scales);
+  if (mode == kQuantMxfp8)
+    k_quant_mx<false><<<(unsigned)rows, 256, 0, st>>>(h, I, codes, bscales, scales);
+  else
+    k_requant<<<(unsigned)rows, 256, 0, st>>>(h, I, mode == kQuantBf16 ? 1 : 0, codes, scales);
   return hipGetLastError();
 }
 

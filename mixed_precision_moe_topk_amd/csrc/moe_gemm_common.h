@@ -11,6 +11,8 @@
 //   * MXFP4 x FP8 : scaled MFMA, A = E4M3 token codes (scale 1), B = E2M1
 //                   weights with their E8M0 scales; the token scale is applied
 //                   in the epilogue.
+//   * MXFP4 x MXFP8: the same MFMA with the activations' E8M0 block scales as
+//                   its A scale operand (no epilogue scale).
 //   * MXFP4 x BF16: weights expanded to bf16 in registers with the E8M0 scale
 //                   folded in (exact), then bf16 MFMA 16x16x32.
 //   * INT4 x FP8  : INT4 codes mapped to E4M3 (exact) in registers, one FP8
@@ -40,6 +42,10 @@ struct Frag;
 template <>
 struct Frag<kMxfp4Fp8> {
   static constexpr int kA = 2;  // uint4 per A row fragment
+};
+template <>
+struct Frag<kMxfp4Mxfp8> {
+  static constexpr int kA = 2;
 };
 template <>
 struct Frag<kInt4Fp8> {

@@ -13,6 +13,7 @@ template <int V, bool FC1, int WAVES_M, int WM, int WN>
 __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int NA = Frag<V>::kA;
+  constexpr bool MXA = a_blockscaled(V);
   static_assert(!FC1 || WN % 2 == 0, "FC1 pairs gate/up tiles");
   Tile tile;
   int nt;
@@ -36,15 +37,19 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   // A row pointers (rows past the tile end re-read its last row; their
   // outputs are never stored)
   const uint8_t* arow[WM];
+  const uint8_t* asrow[WM];
 #pragma unroll
   for (int i = 0; i < WM; ++i) {
     const int r = min(row_base + 16 * i + (lane & 15), row_end - 1);
     const int64_t src = FC1 ? (int64_t)p.row_token[r] : (int64_t)r;
     int64_t off;
-    if (V == kMxfp4Fp8) off = 16 * (lane >> 4);
+    if (fp8_x_fp4(V)) off = 16 * (lane >> 4);
     else if (V == kInt4Fp8) off = 32 * (lane >> 4);
     else off = 64 * (lane >> 4);  // bf16: 32 elements * 2 bytes
     arow[i] = p.a + src * p.a_stride + off;
+    // MXFP8: lane l supplies the E8M0 scales of its row for k-block l/16
+    // (one dword per four steps, byte = step % 4)
+    if (a_blockscaled(V)) asrow[i] = p.a_scale + src * p.a_scale_stride + 4 * (lane >> 4);
   }
 
   v4f acc[WM][WN];
@@ -56,14 +61,18 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   uint4 ac[WM][NA], an[WM][NA];
   uint4 bc[WN], bn[WN];
   uint32_t scc[WN], scn[WN];  // E8M0 dword (MXFP4) or float bits (INT4 group scale)
+  uint32_t asc[WM], asn[WM];  // E8M0 A scale of this lane's row and k-block (MXFP8)
 
-  auto load = [&](int ks, uint4 (&a)[WM][NA], uint4 (&b)[WN], uint32_t (&sc)[WN]) {
+  auto load = [&](int ks, uint4 (&a)[WM][NA], uint4 (&b)[WN], uint32_t (&sc)[WN],
+                  uint32_t (&as)[WM]) {
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       if (i < nvalid) {
-        if (V == kMxfp4Fp8) {
+        if (fp8_x_fp4(V)) {
           a[i][0] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep);
           a[i][1] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep + 64);
+          if (a_blockscaled(V))
+            as[i] = *reinterpret_cast<const uint32_t*>(asrow[i] + 16 * (ks >> 2));
         } else if (V == kInt4Fp8) {
           a[i][0] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep);
           a[i][1] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep + 16);
@@ -87,8 +96,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   };
 
   auto compute = [&](int ks, const uint4 (&a)[WM][NA], const uint4 (&b)[WN],
-                     const uint32_t (&sc)[WN]) {
-    if (V == kMxfp4Fp8) {
+                     const uint32_t (&sc)[WN], const uint32_t (&as)[WM]) {
+    if (fp8_x_fp4(V)) {
       v8i bop[WN];
 #pragma unroll
       for (int j = 0; j < WN; ++j) bop[j] = fp4_operand(b[j]);
@@ -96,14 +105,15 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
       for (int i = 0; i < WM; ++i) {
         if (i < nvalid) {
           const v8i aop = as_v8i(a[i][0], a[i][1]);
+          const int sa = MXA ? (int)as[i] : 127;
 #pragma unroll
           for (int j = 0; j < WN; ++j) {
             if (j >= jvalid) continue;
             switch (ks & 3) {
-              case 0: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, 127, 0, (int)sc[j]); break;
-              case 1: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, 127, 1, (int)sc[j]); break;
-              case 2: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, 127, 2, (int)sc[j]); break;
-              default: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, 127, 3, (int)sc[j]); break;
+              case 0: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, sa, 0, (int)sc[j]); break;
+              case 1: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, MXA ? 1 : 0, sa, 1, (int)sc[j]); break;
+              case 2: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, MXA ? 2 : 0, sa, 2, (int)sc[j]); break;
+              default: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, MXA ? 3 : 0, sa, 3, (int)sc[j]); break;
             }
           }
         }
@@ -147,13 +157,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     }
   };
 
-  load(0, ac, bc, scc);
+  load(0, ac, bc, scc, asc);
   for (int ks = 0; ks < KS; ks += 2) {
-    if (ks + 1 < KS) load(ks + 1, an, bn, scn);
-    compute(ks, ac, bc, scc);
+    if (ks + 1 < KS) load(ks + 1, an, bn, scn, asn);
+    compute(ks, ac, bc, scc, asc);
     if (ks + 1 < KS) {
-      if (ks + 2 < KS) load(ks + 2, ac, bc, scc);
-      compute(ks + 1, an, bn, scn);
+      if (ks + 2 < KS) load(ks + 2, ac, bc, scc, asc);
+      compute(ks + 1, an, bn, scn, asn);
     }
   }
 
@@ -181,6 +191,8 @@ hipError_t launch_gemm_direct(int variant, bool fc1, int cfg, const GemmParams& 
                                : launch_v<kMxfp4Fp8, false>(cfg, p, blocks, st);
     case kMxfp4Bf16: return fc1 ? launch_v<kMxfp4Bf16, true>(cfg, p, blocks, st)
                                 : launch_v<kMxfp4Bf16, false>(cfg, p, blocks, st);
+    case kMxfp4Mxfp8: return fc1 ? launch_v<kMxfp4Mxfp8, true>(cfg, p, blocks, st)
+                                 : launch_v<kMxfp4Mxfp8, false>(cfg, p, blocks, st);
     default: return fc1 ? launch_v<kInt4Fp8, true>(cfg, p, blocks, st)
                         : launch_v<kInt4Fp8, false>(cfg, p, blocks, st);
   }

@@ -1,6 +1,8 @@
 // LDS-staged grouped GEMMs of the fused MoE for E4M3 activations (gfx950):
-// MXFP4 x FP8 on the block-scaled MFMA, INT4 x FP8 with codes mapped to E4M3
-// in registers and the group scale applied after each 128-wide K step.
+// MXFP4 x FP8 on the block-scaled MFMA (per-token activation scales applied
+// in the epilogue, or MXFP8 block scales as the MFMA's A scales), INT4 x FP8
+// with codes mapped to E4M3 in registers and the group scale applied after
+// each 128-wide K step.
 #include "moe_gemm_common.h"
 
 #ifndef MOE_INTERLEAVE
@@ -51,7 +53,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
   constexpr int NB = (PB == 1) ? 2 : 4;  // weight register sets (prefetch distance PB)
   constexpr int AS = (AD == 2) ? 2 : 4;  // A staging register sets (prefetch distance AD)
 
-  static_assert(V == kMxfp4Fp8 || V == kInt4Fp8, "E4M3 activations only");
+  static_assert(fp8_x_fp4(V) || V == kInt4Fp8, "E4M3 activations only");
   static_assert(!FC1 || WN % 2 == 0, "FC1 pairs gate/up tiles");
   constexpr int NT = kWave * NW;           // threads per block
   constexpr int WAVES_N = NW / WAVES_M;
@@ -60,7 +62,8 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
   static_assert((BM * 8) % NT == 0, "A stage must split evenly over the threads");
   constexpr int ABUF = BM * kKStep;        // bytes of one A stage
   constexpr int NCH = BM * 8 / NT;         // 16-byte chunks per thread per stage
-  constexpr bool MX = V == kMxfp4Fp8;
+  constexpr bool MX = fp8_x_fp4(V);
+  constexpr bool MXA = a_blockscaled(V);
 
   // wave-uniform values are made scalar so that branches on them are scalar
   // branches (exec-masked branches make the compiler drain every outstanding
@@ -96,7 +99,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
     const int64_t src = FC1 ? (int64_t)p.row_token[rr] : (int64_t)rr;
     asrc[u] = p.a + src * p.a_stride + 16 * c;
     int g, h;
-    if (V == kMxfp4Fp8) { g = c & 3; h = c >> 2; }   // k = 64h + 16g + [0,16)
+    if (MX) { g = c & 3; h = c >> 2; }               // k = 64h + 16g + [0,16)
     else { g = c >> 1; h = c & 1; }                  // k = 32g + 16h + [0,16)
     const int rho = r & 15;
     adst[u] = ((r >> 4) * 2 + h) * 1024 + (16 * g + (rho ^ ((2 * g + h) | ((rho & 1) << 3)))) * 16;
@@ -105,6 +108,17 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
   const int rho_l = lane & 15, g_l = lane >> 4;
   const int rd0 = (16 * g_l + (rho_l ^ ((2 * g_l) | ((rho_l & 1) << 3)))) * 16;
   const int rd1 = 1024 + (16 * g_l + (rho_l ^ ((2 * g_l + 1) | ((rho_l & 1) << 3)))) * 16;
+  // MXFP8: this lane's A scale dwords (row of subtile i, k-block lane/16),
+  // one per four steps like the weights' scale words
+  const uint8_t* ascl[WM];
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+    if constexpr (MXA) {
+      const int r = min(row_base + 16 * i + rho_l, row_end - 1);
+      const int64_t src = FC1 ? (int64_t)p.row_token[r] : (int64_t)r;
+      ascl[i] = p.a_scale + src * p.a_scale_stride + 4 * g_l;
+    }
+  }
 
   v4f acc[WM][WN];
 #pragma unroll
@@ -116,6 +130,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
   uint4 bq[NB][WN];
   uint32_t sq[NB][WN];         // INT4 group scales, one set per B register set
   uint32_t sx[WN], sx_next[WN];  // MXFP4 scale words of this / the next 4 steps
+  uint32_t ax[WM], ax_next[WM];  // MXFP8 A scale dwords of this / the next 4 steps
 
   auto load_a = [&](int ks, v4u (&dst)[NCH]) __attribute__((always_inline)) {
 #pragma unroll
@@ -144,6 +159,11 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
       const int64_t nb = min(nb0 + j, nb_last);
       sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS4 + (ks >> 2)) * 64 + lane) * 4);
     }
+    if constexpr (MXA) {
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+        ax_next[i] = *reinterpret_cast<const uint32_t*>(ascl[i] + 16 * (ks >> 2));
+    }
   };
 
   // K step ks with S = ks % 4 (E8M0 byte select and register-set index).
@@ -156,6 +176,10 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
     if constexpr (MX && S == 0) {
 #pragma unroll
       for (int j = 0; j < WN; ++j) sx[j] = sx_next[j];
+      if constexpr (MXA) {
+#pragma unroll
+        for (int i = 0; i < WM; ++i) ax[i] = ax_next[i];
+      }
     }
     load_a(min(ks + AD, KS - 1), ast[(S + AD) % AS]);
     load_b(min(ks + PB, KS - 1), bq[(S + PB) % NB], sq[(S + PB) % NB]);
@@ -170,7 +194,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
     v8i bop[WN];
 #pragma unroll
     for (int j = 0; j < WN; ++j)
-      bop[j] = (V == kMxfp4Fp8) ? fp4_operand(bq[S % NB][j]) : int4_operand(bq[S % NB][j]);
+      bop[j] = MX ? fp4_operand(bq[S % NB][j]) : int4_operand(bq[S % NB][j]);
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       if (FULL || (cols && i < nvalid)) {
@@ -179,9 +203,9 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
         const v8i aop = as_v8i(lo, hi);
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
-          if (V == kMxfp4Fp8) {
+          if (MX) {
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                aop, bop[j], acc[i][j], 0, 4, 0, 127, S, (int)sx[j]);
+                aop, bop[j], acc[i][j], 0, 4, MXA ? S : 0, MXA ? (int)ax[i] : 127, S, (int)sx[j]);
           } else {
             const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 aop, bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
@@ -195,7 +219,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
 #if MOE_INTERLEAVE
     // issue order inside the step: the wave's global loads and LDS reads are
     // spread between its MFMAs so they issue while the matrix pipe is busy
-    if (FULL) interleave_schedule<WM * WN, (MX ? (LOAD_SX ? 2 : 1) : 2) * WN + NCH, 2 * WM>();
+    if (FULL) interleave_schedule<WM * WN, (MX ? (LOAD_SX ? 2 : 1) : 2) * WN + NCH + (LOAD_SX && MXA ? WM : 0), 2 * WM>();
 #endif
     __builtin_amdgcn_sched_barrier(0);
     // A of step ks+1 (a harmless copy of the last step once past the end)
@@ -467,13 +491,15 @@ __global__ __launch_bounds__(kWave * NW, MINB) void k_gemm_ab(GemmParams p) {
 }
 
 // ----------------------------------------------------------------------------
-// Direct-to-LDS grouped GEMM for MXFP4 x FP8, 160 x 512 block tiles.
+// Direct-to-LDS grouped GEMM for MXFP4 x FP8, 160 x 512 block tiles (WM = 5).
 // 8 waves (2 x 4), each 80 rows x 128 device columns (5 x 8 MFMA tiles), so
 // one K step reads 18 KB of operands from LDS per 40 MFMAs per wave (40%
 // less LDS traffic per MFMA than 64 x 64 wave tiles).  160-row tiles
 // let one tile hold an expert of up to 160 rows: a tile costs about the same
 // whether full or not (its weight stream dominates), so fewer tiles per
-// expert is what counts.
+// expert is what counts.  With MXFP8 activations the waves also need the
+// activation scales in registers, which 5 x 8 tiles leave no room for, so
+// that variant runs 128 x 512 tiles (4 x 8 per wave).
 // Operands reach LDS by global_load_lds (16 bytes per lane, lane L of a wave
 // instruction lands at M0 + 16 L; an SALU write of M0 needs one wait state
 // before the load reads it), so no staging registers are needed:
@@ -482,8 +508,11 @@ __global__ __launch_bounds__(kWave * NW, MINB) void k_gemm_ab(GemmParams p) {
 //   weights 3 stages x 32 KB  16-column block b at b KB, in device order
 //   scales  2 slots x 8 KB (one 4-step group of E8M0 words each), block b
 //           at 256 b
+//   MXFP8 activation scales  2 slots x 3 KB (one 4-step group each): tile row
+//           r's 16 bytes at 16 r, loaded by waves 0-2 (64 rows each)
 // Step ks issues A of ks+1, weights of ks+2 and, at the
-// start of a 4-step group, the next group's MXFP4 scale words; the wave then
+// start of a 4-step group, the next group's MXFP4 scale words (and, before
+// the A loads, the next group's activation scales); the wave then
 // waits until its loads of step ks+1 have landed (the vector memory counter
 // counts these loads in issue order) and joins the block barrier.  Every
 // load's step index is clamped to the last step, so the number of loads per
@@ -493,16 +522,25 @@ __global__ __launch_bounds__(kWave * NW, MINB) void k_gemm_ab(GemmParams p) {
 // epilogue (an LDS write landing after the block exits would corrupt the next
 // block's LDS).
 namespace dma {
-constexpr int kNW = 8, kWM = 5, kWN = 8, kWavesN = 4;
-constexpr int kBM = 2 * 16 * kWM, kBNB = kWavesN * kWN;  // rows, 16-column blocks per tile
-constexpr int kRG = kBM / 16;           // 16-row groups (wave w loads w and w + 8)
+constexpr int kNW = 8, kWN = 8, kWavesN = 4;
+constexpr int kBNB = kWavesN * kWN;     // 16-column blocks per tile
 constexpr int kBPW = kBNB / kNW;        // weight blocks loaded per wave
-static_assert(kRG >= kNW && kRG <= 2 * kNW, "row groups per wave");
 static_assert(kBPW * kNW == kBNB, "weight blocks per wave");
-constexpr int kABuf = kBM * kKStep, kBBuf = kBNB * 1024;
-constexpr int kAOff = 0, kBOff = 2 * kABuf, kSOff = kBOff + 3 * kBBuf;
-constexpr int kSxSlot = kBNB * 256;
-constexpr int kLdsBytes = kSOff + 2 * kSxSlot;
+constexpr int kBBuf = kBNB * 1024, kSxSlot = kBNB * 256;
+// LDS map of a tile whose waves own WM 16-row subtiles each (MXA: with the
+// activation-scale slots)
+template <int WM, bool MXA>
+struct Map {
+  static constexpr int kBM = 2 * 16 * WM;   // tile rows
+  static constexpr int kRG = kBM / 16;      // 16-row groups (wave w loads w and w + 8)
+  static_assert(kRG >= kNW && kRG <= 2 * kNW, "row groups per wave");
+  static constexpr int kABuf = kBM * kKStep;
+  static constexpr int kAOff = 0, kBOff = 2 * kABuf, kSOff = kBOff + 3 * kBBuf;
+  static constexpr int kAsDma = (kBM + 63) / 64;  // activation-scale loads per group (waves 0..)
+  static constexpr int kAsSlot = kAsDma * 1024, kAsOff = kSOff + 2 * kSxSlot;
+  static constexpr int kBytes = kAsOff + (MXA ? 2 * kAsSlot : 0);
+  static_assert(kBytes <= 160 * 1024, "LDS of one CU");
+};
 }  // namespace dma
 
 __device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_addr) {
@@ -526,12 +564,14 @@ __device__ __forceinline__ void wait_barrier() {
 // One code path for full and partial tiles: the per-subtile checks are scalar
 // branches, which also keep the compiler from hoisting every fragment read of
 // a step (a branch-free full-tile path needed more than 256 registers here).
-template <int V, bool FC1>
+template <int V, bool FC1, int WM>
 __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds, const Tile tile,
                                               const int nt) {
   using namespace dma;
-  static_assert(V == kMxfp4Fp8, "MXFP4 weights x E4M3 activations only");
-  constexpr int WM = kWM, WN = kWN;
+  static_assert(fp8_x_fp4(V), "MXFP4 weights x E4M3 activations only");
+  constexpr bool MXA = a_blockscaled(V);
+  constexpr int WN = kWN;
+  using L = Map<WM, MXA>;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = lane_id();
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int row_end = tile.row0 + tile.nrows;
@@ -550,9 +590,9 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
 
   // A: this wave loads fragments (g, 0) and (g, 1) of row groups g = wave and
-  // (waves below kRG - 8) g = wave + 8: row 16 g + L%16 of the tile (the
+  // (waves below L::kRG - 8) g = wave + 8: row 16 g + L%16 of the tile (the
   // last row repeated past the end), operand piece L/16
-  const bool two_rg = wave < kRG - kNW;  // compile-time false when kRG == kNW
+  const bool two_rg = wave < L::kRG - kNW;  // compile-time false when L::kRG == kNW
   const int kofs = 16 * (lane >> 4);
   const int ar0 = min(tile.row0 + 16 * wave + (lane & 15), row_end - 1);
   const int ar1 = min(tile.row0 + 16 * (wave + kNW) + (lane & 15), row_end - 1);
@@ -565,7 +605,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   for (int u = 0; u < kBPW; ++u) wcol[u] = wbase + min(nbb + kBPW * wave + u, nb_last) * KS * 1024;
 
   auto issue_a = [&](int ks, int stage) __attribute__((always_inline)) {
-    const uint32_t dst = lds0 + kAOff + stage * kABuf + wave * 2048;
+    const uint32_t dst = lds0 + L::kAOff + stage * L::kABuf + wave * 2048;
     lds_dma16(arow0 + ks * kKStep, dst);
     lds_dma16(arow0 + ks * kKStep + kAHalf, dst + 1024);
     if (two_rg) {
@@ -574,15 +614,27 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
     }
   };
   auto issue_b = [&](int ks, int stage) __attribute__((always_inline)) {
-    const uint32_t dst = lds0 + kBOff + stage * kBBuf + wave * kBPW * 1024;
+    const uint32_t dst = lds0 + L::kBOff + stage * kBBuf + wave * kBPW * 1024;
 #pragma unroll
     for (int u = 0; u < kBPW; ++u) lds_dma16_s(wcol[u] + ks * 1024, lane * 16, dst + u * 1024);
+  };
+  // MXFP8: wave w < L::kAsDma loads the activation-scale group of tile rows
+  // 64 w + L (the last row repeated past the end); a 32-bit offset from the
+  // scale array (its size is checked on the host) saves a register pair
+  uint32_t asoff = 0;
+  if constexpr (MXA) {
+    const int r = min(tile.row0 + 64 * min(wave, L::kAsDma - 1) + lane, row_end - 1);
+    asoff = (uint32_t)((FC1 ? (int64_t)p.row_token[r] : (int64_t)r) * p.a_scale_stride);
+  }
+  auto issue_as = [&](int grp, int slot) __attribute__((always_inline)) {
+    if (MXA && wave < L::kAsDma)
+      lds_dma16_s(p.a_scale, asoff + 16 * grp, lds0 + L::kAsOff + slot * L::kAsSlot + wave * 1024);
   };
   auto issue_sx = [&](int grp, int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kBPW; ++u) {
       const uint8_t* src = sbase + (min(nbb + kBPW * wave + u, nb_last) * KS4 + grp) * 256;
-      lds_dma4_s(src, lane * 4, lds0 + kSOff + slot * kSxSlot + (wave * kBPW + u) * 256);
+      lds_dma4_s(src, lane * 4, lds0 + L::kSOff + slot * kSxSlot + (wave * kBPW + u) * 256);
     }
   };
 
@@ -597,32 +649,39 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   // weights (kBPW) and, at the start of a group, the scale words (kBPW)
   auto step = [&](auto s_c, int ks, int bstage) __attribute__((always_inline)) {
     constexpr int S = decltype(s_c)::value;
+    if constexpr (MXA && S == 0) issue_as(min((ks >> 2) + 1, KS4 - 1), ((ks >> 2) + 1) & 1);
     issue_a(min(ks + 1, KS - 1), (S + 1) & 1);
     issue_b(min(ks + 2, KS - 1), bstage == 0 ? 2 : bstage - 1);
     if constexpr (S == 0) issue_sx(min((ks >> 2) + 1, KS4 - 1), ((ks >> 2) + 1) & 1);
-    const uint8_t* bs = lds + kBOff + bstage * kBBuf + (wn * WN) * 1024 + lane * 16;
+    const uint8_t* bs = lds + L::kBOff + bstage * kBBuf + (wn * WN) * 1024 + lane * 16;
     if constexpr (S == 0) {
-      const uint8_t* ss = lds + kSOff + ((ks >> 2) & 1) * kSxSlot + (wn * WN) * 256 + lane * 4;
+      const uint8_t* ss = lds + L::kSOff + ((ks >> 2) & 1) * kSxSlot + (wn * WN) * 256 + lane * 4;
 #pragma unroll
       for (int j = 0; j < WN; ++j) sx[j] = *reinterpret_cast<const uint32_t*>(ss + j * 256);
     }
+    // MXFP8: A scale dword of subtile i (row lane%16, k-block lane/16), read
+    // per step next to its operands (held across a group it costs the
+    // registers this tile does not have)
+    const uint8_t* sa = lds + L::kAsOff + ((ks >> 2) & 1) * L::kAsSlot +
+                        (16 * WM * wm + (lane & 15)) * 16 + 4 * (lane >> 4);
     v8i bop[WN];
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
       const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
       bop[j] = fp4_operand(b);
     }
-    const uint8_t* as = lds + kAOff + (S & 1) * kABuf + (wm * WM) * 2048 + lane * 16;
+    const uint8_t* as = lds + L::kAOff + (S & 1) * L::kABuf + (wm * WM) * 2048 + lane * 16;
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       if (cols && i < nvalid) {
         const uint4 lo = *reinterpret_cast<const uint4*>(as + i * 2048);
         const uint4 hi = *reinterpret_cast<const uint4*>(as + i * 2048 + 1024);
         const v8i aop = as_v8i(lo, hi);
+        const int ax = MXA ? *reinterpret_cast<const int*>(sa + i * 256) : 127;
 #pragma unroll
         for (int j = 0; j < WN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              aop, bop[j], acc[i][j], 0, 4, 0, 127, S, (int)sx[j]);
+              aop, bop[j], acc[i][j], 0, 4, MXA ? S : 0, ax, S, (int)sx[j]);
       }
     }
     // the loads of step ks+1 (A issued above, weights one step earlier) have
@@ -631,6 +690,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   };
 
   // prologue: A and weights (and scales) of step 0, weights of step 1
+  issue_as(0, 0);
   issue_a(0, 0);
   issue_b(0, 0);
   issue_sx(0, 0);
@@ -654,19 +714,20 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   epilogue<FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
-template <int V, bool FC1>
+template <int V, bool FC1, int WM>
 __global__ __launch_bounds__(dma::kNW * kWave, 1) void k_gemm_dma(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[dma::kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[dma::Map<WM, a_blockscaled(V)>::kBytes];
   Tile tile;
   int nt;
   if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
-  gemm_dma_body<V, FC1>(p, lds, tile, nt);
+  gemm_dma_body<V, FC1, WM>(p, lds, tile, nt);
 }
 
 template <int V, bool FC1>
 static hipError_t launch_v(int cfg, const GemmParams& p, int64_t blocks, hipStream_t st) {
   if (cfg == 1) k_gemm_lds<V, FC1, 4, 1, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p);
-  else if constexpr (V == kMxfp4Fp8) k_gemm_dma<V, FC1><<<(unsigned)blocks, dma::kNW * kWave, 0, st>>>(p);
+  else if constexpr (fp8_x_fp4(V))  // 160 x 512; 128 x 512 with MXFP8 scales (registers)
+    k_gemm_dma<V, FC1, a_blockscaled(V) ? 4 : 5><<<(unsigned)blocks, dma::kNW * kWave, 0, st>>>(p);
   else k_gemm_ab<V, FC1, 8, 2, 4, 4><<<(unsigned)blocks, 512, 0, st>>>(p);
   return hipGetLastError();
 }
@@ -679,6 +740,8 @@ hipError_t launch_gemm_lds(int variant, bool fc1, int cfg, const GemmParams& p,
   switch (variant) {
     case kMxfp4Fp8: return fc1 ? launch_v<kMxfp4Fp8, true>(cfg, p, blocks, st)
                                : launch_v<kMxfp4Fp8, false>(cfg, p, blocks, st);
+    case kMxfp4Mxfp8: return fc1 ? launch_v<kMxfp4Mxfp8, true>(cfg, p, blocks, st)
+                                 : launch_v<kMxfp4Mxfp8, false>(cfg, p, blocks, st);
     case kInt4Fp8: return fc1 ? launch_v<kInt4Fp8, true>(cfg, p, blocks, st)
                               : launch_v<kInt4Fp8, false>(cfg, p, blocks, st);
     default: return hipErrorInvalidValue;

@@ -7,6 +7,7 @@ import numpy as np
 import moe_inputs as MI
 import oracle as O
 from oracle import formats as F
+from oracle import quant as Q
 
 
 def rel_l2(a, b):
@@ -86,11 +87,19 @@ class Problem:
         r["offsets"] = view(L.offsets, np.int32, wl.experts + 1)
         r["row_token"] = view(L.row_token, np.int32, rows)
         r["slot_row"] = view(L.slot_row, np.int32, rows).reshape(T, k)
-        if wl.afmt == "fp8":
+        e4m3 = wl.afmt in ("fp8", "mxfp8")
+        if e4m3:
             r["token_codes"] = view(L.tok_codes, np.uint8, T * wl.hidden).reshape(T, wl.hidden)
             r["token_scales"] = view(L.tok_scales, np.float32, T)
+        if wl.afmt == "mxfp8":
+            rb = mx_scale_row_bytes(wl.hidden)
+            r["token_block_scales"] = mx_scales_canonical(
+                view(L.tok_bscales, np.uint8, T * rb).reshape(T, rb), wl.hidden)
+            rb = mx_scale_row_bytes(wl.inter)
+            r["fc2_block_scales"] = mx_scales_canonical(
+                view(L.fc2_bscales, np.uint8, rows * rb).reshape(rows, rb), wl.inter)
         r["h"] = view(L.h, np.float32, rows * wl.inter).reshape(rows, wl.inter)
-        qdt = np.uint8 if wl.afmt == "fp8" else np.uint16
+        qdt = np.uint8 if e4m3 else np.uint16
         r["fc2_codes"] = view(L.fc2_codes, qdt, rows * wl.inter).reshape(rows, wl.inter)
         r["fc2_scales"] = view(L.fc2_scales, np.float32, rows)
         r["y2"] = view(L.y2, np.float32, rows * wl.hidden).reshape(rows, wl.hidden)
@@ -127,6 +136,19 @@ class Problem:
         return O.forward(hb, lg, wl.top_k, lambda e: self.oracle_w[e], wl.wfmt, wl.afmt)
 
 
+def mx_scale_row_bytes(cols):
+    """Bytes per row of the library's MXFP8 block scales (16 per 512 columns)."""
+    return 16 * ((cols + 511) // 512)
+
+
+def mx_scales_canonical(stored, cols):
+    """Library MXFP8 block scales [rows, mx_scale_row_bytes(cols)], kept in the
+    matrix cores' order (block b at byte 16*(b//16) + 4*(b%4) + (b//4)%4), as
+    the canonical [rows, cols/32] row-major E8M0 codes."""
+    b = np.arange(cols // 32)
+    return stored[:, 16 * (b >> 4) + 4 * (b & 3) + ((b >> 2) & 3)]
+
+
 def expected_work_map(offsets, tile_m):
     """GEMM work map from the per-expert row ranges: (expert, row0, nrows) of
     every tile, in expert order; each expert's rows are cut into tile_m-row
@@ -149,12 +171,24 @@ def compare_all(g, r, wl, exact_rows=True):
     if wl.afmt == "fp8":
         assert np.array_equal(g["token_codes"], r["token_codes"]), "token E4M3 codes differ"
         assert np.array_equal(g["token_scales"].view(np.uint32), r["token_scales"].view(np.uint32))
+    if wl.afmt == "mxfp8":
+        assert np.array_equal(g["token_codes"], r["token_codes"]), "token E4M3 codes differ"
+        assert np.array_equal(g["token_block_scales"], r["token_block_scales"]), "token E8M0 differ"
     assert rel_l2(g["h"], r["h"]) <= 1e-4, rel_l2(g["h"], r["h"])
+    # FC2 input: h differs from the oracle's by float32 rounding, so a few
+    # codes (and, rarely, a block exponent at a power-of-two boundary) differ
     if wl.afmt == "fp8":
         same = np.mean(g["fc2_codes"] == r["fc2_codes"])
         assert same > 0.97, same
         dq = F.e4m3_decode(g["fc2_codes"]) * g["fc2_scales"][:, None]
         dr = F.e4m3_decode(r["fc2_codes"]) * r["fc2_scales"][:, None]
+        assert rel_l2(dq, dr) <= 1e-3
+    if wl.afmt == "mxfp8":
+        same = np.mean(g["fc2_codes"] == r["fc2_codes"])
+        assert same > 0.97, same
+        assert np.mean(g["fc2_block_scales"] == r["fc2_block_scales"]) > 0.99
+        dq = Q.mxfp8_decode(g["fc2_codes"], g["fc2_block_scales"])
+        dr = Q.mxfp8_decode(r["fc2_codes"], r["fc2_block_scales"])
         assert rel_l2(dq, dr) <= 1e-3
     assert rel_l2(g["y2"], r["y2"]) <= 2e-3, rel_l2(g["y2"], r["y2"])
     return check_output(g["out"], r["out"])

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == set(M.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 def _d(**kw):
@@ -50,7 +50,8 @@ def test_weight_sizes(L):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(hidden=100), 1), (dict(inter=0), 1), (dict(num_experts=0), 1),
-    (dict(num_experts=2000), 1), (dict(wfmt="int4", afmt="bf16"), 2)])
+    (dict(num_experts=2000), 1), (dict(wfmt="int4", afmt="bf16"), 2),
+    (dict(wfmt="int4", afmt="mxfp8"), 2)])
 def test_bad_dims(L, kw, status):
     with pytest.raises(M.MoeError) as ei:
         M.weights_query(_d(**kw))
@@ -96,6 +97,21 @@ def test_workspace_layout_regions(L):
     assert lay.y2 + 4096 * 8 * 7168 * 4 <= lay.total
     assert lay.tile_m == 160 and lay.gemm_cfg == 2
     assert M.workspace_layout(_d(), 64, 8).tile_m == 16
+
+
+def test_workspace_layout_mxfp8(L):
+    # MXFP8: E4M3 codes for tokens and FC2 inputs plus E8M0 block scales in
+    # 16-byte groups per 512 columns (hidden 7168 -> 224 B, inter 2048 -> 64 B)
+    lay = M.workspace_layout(_d(afmt="mxfp8"), 4096, 8)
+    assert lay.tok_bscales % 256 == 0 and lay.fc2_bscales % 256 == 0
+    assert lay.fc2_bscales >= lay.tok_bscales + 4096 * 224
+    assert lay.fc2_bscales + 4096 * 8 * 64 <= lay.total
+    assert lay.fc2_codes + 4096 * 8 * 2048 <= lay.fc2_scales  # one byte per code
+    assert lay.tile_m == 128 and lay.gemm_cfg == 2
+    # 384 columns: one partial group of 16 bytes per row
+    lay = M.workspace_layout(_d(num_experts=8, hidden=384, inter=256, afmt="mxfp8"), 100, 2)
+    assert lay.fc2_bscales - lay.tok_bscales >= 100 * 16
+    assert M.workspace_layout(_d(), 4096, 8).tok_bscales == M.workspace_layout(_d(), 4096, 8).fc2_bscales
 
 
 def test_trace_modes(L):

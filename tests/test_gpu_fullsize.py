@@ -17,7 +17,7 @@ from tests.harness import Problem, check_output, expected_work_map, rel_l2
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 CASES = ["dsv3_decode_mxfp4_bf16", "dsv3_int4_fp8", "dsv3_prefill_mxfp4_fp8",
-         "dsv4pro_prefill_mxfp4_fp8"]
+         "dsv4pro_prefill_mxfp4_fp8", "dsv3_prefill_mxfp4_mxfp8"]
 SAMPLE = 3  # tokens checked against the oracle end to end
 
 
@@ -72,11 +72,15 @@ def test_fullsize_sampled(name):
     assert np.array_equal(g["slot_row"], slot_row.astype(np.int32))
     # GEMM work map (main and tail tiles) from the expert row ranges
     assert np.array_equal(g["tiles"], expected_work_map(off, g["tile_m"]))
-    # per-token E4M3 codes and scales for every token
+    # E4M3 token codes and their scales (per token, or E8M0 per 32) for every token
     if wl.afmt == "fp8":
         q, s = O.quant.e4m3_rows(F.bf16_to_f32(p.hidden))
         assert np.array_equal(g["token_codes"], q)
         assert np.array_equal(g["token_scales"].view(np.uint32), s.view(np.uint32))
+    if wl.afmt == "mxfp8":
+        q, sx = O.quant.mxfp8_rows(F.bf16_to_f32(p.hidden))
+        assert np.array_equal(g["token_codes"], q)
+        assert np.array_equal(g["token_block_scales"], sx)
     # prepared weight codes of two experts
     for e in (p.active[0], p.active[-1]):
         q1, s1, q2, s2 = p.unpack(e, 1)

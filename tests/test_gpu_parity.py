@@ -24,6 +24,13 @@ SMALL = [
     (9, 40, 4, 512, 128, "int4", "fp8", 19, 0.0),
     (1, 3, 3, 128, 128, "mxfp4", "fp8", 20, 0.0),     # single token, k = E
     (6, 1, 1, 8320, 4224, "mxfp4", "fp8", 23, 0.0),   # rows longer than the quantisers keep in registers
+    # MXFP8 activations: every tile configuration, K not a multiple of 512
+    # (a partial 4-step scale group), ragged row and N tails
+    (70, 6, 3, 384, 256, "mxfp4", "mxfp8", 31, 0.0),  # 64-row tiles
+    (300, 5, 2, 256, 384, "mxfp4", "mxfp8", 32, 2.0), # 128-row tiles, tails
+    (400, 4, 2, 384, 640, "mxfp4", "mxfp8", 33, 1.0), # full + ragged 128-row tiles, N tail
+    (9, 40, 4, 512, 128, "mxfp4", "mxfp8", 34, 0.0),  # 16-row tiles, empty experts
+    (6, 1, 1, 8320, 4224, "mxfp4", "mxfp8", 35, 0.0), # long rows, 17 scale groups (last partial)
 ]
 
 
