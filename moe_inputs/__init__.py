@@ -68,6 +68,9 @@ WORKLOADS = {
     # the DeepSeek-V3 prefill shape with MXFP8 activations (E8M0 per 32)
     "dsv3_prefill_mxfp4_mxfp8": Workload("dsv3_prefill_mxfp4_mxfp8", 6, 4096, 256, 8,
                                          7168, 2048, "mxfp4", "mxfp8", 0.0, "mfma"),
+    # the same shape with W4A4: MXFP4 activations (E2M1, E8M0 per 32)
+    "dsv3_prefill_mxfp4_mxfp4": Workload("dsv3_prefill_mxfp4_mxfp4", 7, 4096, 256, 8,
+                                         7168, 2048, "mxfp4", "mxfp4", 0.0, "mfma"),
 }
 
 

@@ -16,14 +16,18 @@ Steps, each rounded only at its storage point:
   route     top-k by float32 logit (ties -> lower expert index), weights =
             softmax over the k selected logits (float64 exp), stored float32.
   quantize  per-token E4M3 (FP8 activations), MXFP8 (E4M3 with one E8M0
-            scale per 32 elements of a token; the token scale is then 1) or
-            the bf16 values (BF16).
+            scale per 32 elements of a token; the token scale is then 1),
+            MXFP4 (W4A4: E2M1 with one E8M0 scale per 32, the weights' own
+            quantiser; PR #4793's walkthrough passes an MXFP4 activation pack
+            and its scales to the fused MoE in its w4a4 mode) or the bf16
+            values (BF16).
   expand    rows grouped by expert, then token, then slot.
   gemm1     acc = A . W1^T exactly in float64; y1 = fl32(acc * token scale).
   swiglu    h = fl32(silu(gate) * up), gate = y1[:, :I], up = y1[:, I:],
             silu(g) = g / (1 + exp(-g)).
   fc2 input FP8: per-row E4M3 of h (same quantiser as the tokens);
-            MXFP8: per-row MXFP8 of h (row scale 1); BF16: bf16(h), scale 1.
+            MXFP8 / MXFP4: per-row MXFP8 / MXFP4 of h (row scale 1); BF16:
+            bf16(h), scale 1.
   gemm2     acc2 = A2 . W2^T in float64; y2 = fl32(acc2 * row scale).
   finalize  out[t] = bf16(sum_j fl32(w[t,j] * y2[row(t,j)])), the sum kept
             in float32 and taken in slot order.
@@ -127,6 +131,12 @@ def forward(hidden_bits: np.ndarray, logits: np.ndarray, top_k: int,
         q, sx_tok = Q.mxfp8_rows(x)
         s_tok = np.ones(t, dtype=np.float32)
         a_dec = Q.mxfp8_decode(q, sx_tok)
+    elif afmt == "mxfp4":
+        # W4A4: activations in the weights' own MXFP4 format (E2M1 elements,
+        # E8M0 per 32, the OCP MX rule), packed two codes per byte
+        q, sx_tok = Q.mxfp4_quantize(x)
+        s_tok = np.ones(t, dtype=np.float32)
+        a_dec = Q.mxfp4_decode(q, sx_tok)
     elif afmt == "bf16":
         q, s_tok = None, np.ones(t, dtype=np.float32)
         a_dec = x.astype(np.float64)
@@ -147,9 +157,10 @@ def forward(hidden_bits: np.ndarray, logits: np.ndarray, top_k: int,
             inter = w1.shape[0] // 2
             h_all = np.zeros((rows, inter), dtype=np.float32)
             y2 = np.zeros((rows, h), dtype=np.float32)
-            q2 = np.zeros((rows, inter), dtype=np.uint16 if afmt == "bf16" else np.uint8)
+            q2 = np.zeros((rows, inter // 2 if afmt == "mxfp4" else inter),
+                          dtype=np.uint16 if afmt == "bf16" else np.uint8)
             s2 = np.ones(rows, dtype=np.float32)
-            if afmt == "mxfp8":
+            if afmt in ("mxfp8", "mxfp4"):
                 sx2 = np.full((rows, inter // Q.MX_BLOCK), 127, dtype=np.uint8)
             if keep_y1:
                 y1_all = np.zeros((rows, 2 * inter), dtype=np.float32)
@@ -157,6 +168,10 @@ def forward(hidden_bits: np.ndarray, logits: np.ndarray, top_k: int,
             assert Q.mx_exponent_spread(wts.w1s) <= 18 and Q.mx_exponent_spread(wts.w2s) <= 18
         if check_exact and wfmt == "mxfp4" and afmt == "mxfp8":
             assert Q.mx_exponent_spread(wts.w1s) + Q.mx_exponent_spread(sx_tok[toks]) <= 18
+        if check_exact and wfmt == "mxfp4" and afmt == "mxfp4":
+            # E2M1 x E2M1 products are multiples of 2^(Xa+Xw-2) below 36 * 2^(Xa+Xw):
+            # K <= 8192 terms stay exact in float64 for an exponent spread <= 32
+            assert Q.mx_exponent_spread(wts.w1s) + Q.mx_exponent_spread(sx_tok[toks]) <= 32
         acc = a_dec[toks] @ w1.T
         y1 = (acc * s_tok[toks][:, None].astype(np.float64)).astype(np.float32)
         if keep_y1:
@@ -173,6 +188,13 @@ def forward(hidden_bits: np.ndarray, logits: np.ndarray, top_k: int,
             sx2[r0:r1] = sxx
             if check_exact and wfmt == "mxfp4":
                 assert Q.mx_exponent_spread(wts.w2s) + Q.mx_exponent_spread(sxx) <= 18
+        elif afmt == "mxfp4":
+            qq, sxx = Q.mxfp4_quantize(hh)
+            ss = np.ones(r1 - r0, dtype=np.float32)
+            a2 = Q.mxfp4_decode(qq, sxx)
+            sx2[r0:r1] = sxx
+            if check_exact and wfmt == "mxfp4":
+                assert Q.mx_exponent_spread(wts.w2s) + Q.mx_exponent_spread(sxx) <= 32
         else:
             qq = F.bf16_rne(hh)
             ss = np.ones(r1 - r0, dtype=np.float32)

@@ -102,7 +102,7 @@ def test_expand_structure():
 # ----------------------------------------------------------------------------- exact GEMMs
 
 @pytest.mark.parametrize("wfmt,afmt", [("mxfp4", "fp8"), ("mxfp4", "bf16"), ("int4", "fp8"),
-                                       ("mxfp4", "mxfp8")])
+                                       ("mxfp4", "mxfp8"), ("mxfp4", "mxfp4")])
 def test_gemms_against_exact_rationals(wfmt, afmt):
     wl = MI.small_workload(tokens=3, experts=4, top_k=2, hidden=128, inter=128,
                            wfmt=wfmt, afmt=afmt, seed=77)
@@ -117,6 +117,10 @@ def test_gemms_against_exact_rationals(wfmt, afmt):
         # element times 2^(code - 127) of its 32-element block, as exact rationals
         a_dec = [[Fraction(float(F.e4m3_decode(c))) * Fraction(2) ** (int(sc[i // 32]) - 127)
                   for i, c in enumerate(row)]
+                 for row, sc in zip(r["token_codes"], r["token_block_scales"])]
+    elif afmt == "mxfp4":
+        a_dec = [[Fraction(float(F.e2m1_decode(c))) * Fraction(2) ** (int(sc[i // 32]) - 127)
+                  for i, c in enumerate(F.unpack_nibbles(row[None])[0])]
                  for row, sc in zip(r["token_codes"], r["token_block_scales"])]
     else:
         a_dec = [[Fraction(float(v)) for v in row] for row in x]
@@ -147,6 +151,10 @@ def test_gemms_against_exact_rationals(wfmt, afmt):
                 sc2 = r["fc2_block_scales"][row]
                 a2 = [Fraction(float(F.e4m3_decode(c))) * Fraction(2) ** (int(sc2[i // 32]) - 127)
                       for i, c in enumerate(r["fc2_codes"][row])]
+            elif afmt == "mxfp4":
+                sc2 = r["fc2_block_scales"][row]
+                a2 = [Fraction(float(F.e2m1_decode(c))) * Fraction(2) ** (int(sc2[i // 32]) - 127)
+                      for i, c in enumerate(F.unpack_nibbles(r["fc2_codes"][row][None])[0])]
             else:
                 a2 = [Fraction(float(v)) for v in F.bf16_to_f32(r["fc2_codes"][row])]
             s2 = Fraction(float(r["fc2_scales"][row]))
@@ -222,8 +230,26 @@ def _torch_mxfp8(x):
     return (dec * torch.pow(2.0, xe)[..., None]).reshape(r, c)
 
 
+def _torch_mxfp4(x):
+    """MXFP4 of float32 rows with torch ops: per 32-element block X =
+    floor(log2 amax) - 2 (torch.frexp), each x / 2^X rounded to the nearest
+    E2M1 magnitude {0, .5, 1, 1.5, 2, 3, 4, 6} (ties to the even code,
+    saturating at 6), returned decoded (float64)."""
+    r, c = x.shape
+    b = x.reshape(r, c // 32, 32).double()
+    amax = b.abs().amax(dim=-1)
+    _, e = torch.frexp(torch.where(amax > 0, amax, torch.ones_like(amax)))
+    xe = torch.where(amax > 0, e.double() - 1 - 2, torch.zeros_like(amax)).clamp(min=-127)
+    v = b / torch.pow(2.0, xe)[..., None]
+    grid = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=torch.float64)
+    dist = (v.abs().clamp(max=6.0)[..., None] - grid).abs()
+    dist = dist + 1e-12 * (torch.arange(8) % 2).double()  # exact ties -> even code
+    mag = grid[dist.argmin(dim=-1)]
+    return (torch.sign(v) * mag * torch.pow(2.0, xe)[..., None]).reshape(r, c)
+
+
 @pytest.mark.parametrize("wfmt,afmt", [("mxfp4", "fp8"), ("mxfp4", "bf16"), ("int4", "fp8"),
-                                       ("mxfp4", "mxfp8")])
+                                       ("mxfp4", "mxfp8"), ("mxfp4", "mxfp4")])
 def test_single_expert_equals_independent_mlp(wfmt, afmt):
     """E = 1, k = 1: out = bf16(MLP(x)) computed here with torch float64 ops on
     the decoded operands (an independent composition of the steps)."""
@@ -242,6 +268,9 @@ def test_single_expert_equals_independent_mlp(wfmt, afmt):
     elif afmt == "mxfp8":
         s = torch.ones(wl.tokens)
         a = _torch_mxfp8(x)
+    elif afmt == "mxfp4":
+        s = torch.ones(wl.tokens)
+        a = _torch_mxfp4(x)
     else:
         s = torch.ones(wl.tokens)
         a = x.double()
@@ -256,6 +285,9 @@ def test_single_expert_equals_independent_mlp(wfmt, afmt):
     elif afmt == "mxfp8":
         s2 = torch.ones(wl.tokens)
         a2 = _torch_mxfp8(hh)
+    elif afmt == "mxfp4":
+        s2 = torch.ones(wl.tokens)
+        a2 = _torch_mxfp4(hh)
     else:
         s2 = torch.ones(wl.tokens)
         a2 = hh.to(torch.bfloat16).double()
