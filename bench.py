@@ -35,12 +35,13 @@ sys.path.insert(0, ROOT)
 import moe_inputs as MI  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "mxfp8": 5000.0, "bf16": 2500.0}
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "mxfp8": 5000.0, "mxfp4": 10100.0, "bf16": 2500.0}
 COPY_CALIB_BYTES = 256 << 20
 METRIC = "fused-MoE tokens/s + % MFMA peak (prefill) / % HBM GB/s (decode), 1 GPU"
-ORACLE_SAMPLE_TOKENS = {"tiny_mxfp4_fp8": 16, "dsv3_decode_mxfp4_bf16": 10,
-                        "dsv3_prefill_mxfp4_fp8": 6, "dsv4pro_prefill_mxfp4_fp8": 6,
-                        "dsv3_int4_fp8": 6, "dsv3_prefill_mxfp4_mxfp8": 6}
+ORACLE_SAMPLE_TOKENS = {"tiny_mxfp4_fp8": 16, "dsv3_decode_mxfp4_bf16": 12,
+                        "dsv3_prefill_mxfp4_fp8": 12, "dsv4pro_prefill_mxfp4_fp8": 24,
+                        "dsv3_int4_fp8": 9, "dsv3_prefill_mxfp4_mxfp8": 12,
+                        "dsv3_prefill_mxfp4_mxfp4": 12}
 CSRC = "mixed_precision_moe_topk_amd/csrc/"
 
 
@@ -80,6 +81,9 @@ def parse():
                     help="draw float32 masters on the device (torch Philox, fast) or with the "
                          "host generator shared with the oracle (slow for 256+ experts)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--autotune", action="store_true",
+                    help="validate and time every GEMM tile configuration on the workload's "
+                         "inputs before the timed region, and run the fastest")
     return ap.parse_args()
 
 
@@ -143,6 +147,13 @@ def main():
     hidden = torch.from_numpy(MI.hidden_bf16(wl.seed, wl.tokens, wl.hidden).view(np.int16)).cuda()
     logits = torch.from_numpy(MI.router_logits(wl.seed, wl.tokens, wl.experts, wl.bias_sigma)).cuda()
     out = torch.empty((wl.tokens, wl.hidden), dtype=torch.int16, device="cuda")
+    default_cfg = M.workspace_layout(d, wl.tokens, wl.top_k).gemm_cfg
+    tuning = None
+    if args.autotune:
+        print("# autotune", file=sys.stderr, flush=True)
+        chosen, cfg_ms = M.autotune(d, hidden, logits, weights, scales, wl.top_k, iters=5)
+        tuning = {"default_cfg": default_cfg, "chosen_cfg": chosen,
+                  "layer_ms_per_cfg": [round(m, 4) for m in cfg_ms]}
     lay = M.workspace_layout(d, wl.tokens, wl.top_k)
     ws = torch.empty(lay.total, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
@@ -225,11 +236,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.afmt == "bf16" else "fp8",  # E4M3 operands (MXFP8 too)
+        # operand type of the matrix products: bf16, E4M3 (FP8, MXFP8) or E2M1 (W4A4)
+        "dtype": {"bf16": "bf16", "mxfp4": "fp4"}.get(wl.afmt, "fp8"),
         "data": "synthetic",
         "config": {"workload": wl.key, "tokens": wl.tokens, "experts": wl.experts,
                    "top_k": wl.top_k, "hidden": wl.hidden, "inter": wl.inter,
                    "weights": wl.wfmt, "activations": wl.afmt, "active_experts": active,
+                   "gemm_cfg": lay.gemm_cfg, "tile_m": lay.tile_m,
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "layer": {"weight_GBps": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),
@@ -237,6 +250,8 @@ def main():
                   "gemm_TFLOPs": round(layer_flops / (ms_per_step / 1e3) / 1e12, 1),
                   "stage_ms": {k: round(v, 4) for k, v in stage_avg.items()}},
     }
+    if tuning is not None:
+        rec["autotune"] = tuning
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wl)

@@ -21,13 +21,15 @@
  *
  * Weight formats: MXFP4 (E2M1 codes, one E8M0 scale per 32 elements along K)
  * or INT4 (symmetric codes, one float32 scale per 128 elements along K).
- * Supported combinations: MXFP4 x FP8, MXFP4 x BF16, INT4 x FP8.
+ * Supported combinations: MXFP4 x FP8, MXFP4 x BF16, INT4 x FP8, and with
+ * block-scaled activations MXFP4 x MXFP8 and MXFP4 x MXFP4 (W4A4).
  *
  * Conventions
  *   - All tensors are dense row-major; "device" pointers are HIP device
  *     memory on the current device; the caller owns every buffer.
  *   - Every call is asynchronous on `stream` unless stated; no call
- *     synchronises the stream or allocates, except moe_run (see below).
+ *     synchronises the stream or allocates, except moe_run and moe_autotune
+ *     (see below).
  *   - Errors are returned as moe_status; moe_last_error() gives a message
  *     for the calling thread.  Nothing is printed and nothing aborts.
  *   - Asynchronous device faults surface at the caller's next
@@ -49,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -64,8 +66,10 @@ typedef enum { MOE_W_MXFP4 = 0, MOE_W_INT4_G128 = 1 } moe_wfmt;
 /* Activations: FP8_TOKEN = E4M3 with one float32 scale per token (and per FC2
  * input row); MXFP8 = E4M3 with one E8M0 scale per 32 consecutive elements of
  * a token (and of an FC2 input row), applied inside the block-scaled MFMA
- * (MXFP4 weights only); BF16 = the activations as given. */
-typedef enum { MOE_A_FP8_TOKEN = 0, MOE_A_BF16 = 1, MOE_A_MXFP8 = 2 } moe_afmt;
+ * (MXFP4 weights only); MXFP4 (W4A4) = E2M1 with one E8M0 scale per 32, the
+ * weights' own quantiser, at the MFMA's FP4 rate (MXFP4 weights only); BF16 =
+ * the activations as given. */
+typedef enum { MOE_A_FP8_TOKEN = 0, MOE_A_BF16 = 1, MOE_A_MXFP8 = 2, MOE_A_MXFP4 = 3 } moe_afmt;
 
 /* Shape and formats of one MoE layer.  W1 is [2*inter, hidden] per expert
  * (rows [0, inter) gate, [inter, 2*inter) up); W2 is [hidden, inter]. */
@@ -85,18 +89,22 @@ typedef struct {
  *   row_token   int32  [T*k]    token of each expanded row (expert-major,
  *                               then token, then slot)
  *   slot_row    int32  [T, k]   expanded row of each (token, slot)
- *   tok_codes   uint8  [T, H]   E4M3 token codes (FP8 and MXFP8 activations)
- *   tok_scales  float  [T]      token scales (FP8 activations only)
+ *   tok_codes   uint8  [T, H]   E4M3 token codes (FP8 and MXFP8 activations);
+ *                      [T, H/2] E2M1 codes, element 2i in the low nibble (MXFP4)
+ *   tok_scales  float  [T]      token scales (FP8 activations; 1.0 for MX formats)
  *   h           float  [T*k, I] SwiGLU output per expanded row
- *   fc2_codes   uint8  [T*k, I] E4M3 (FP8, MXFP8) or bf16 bits ([T*k, I] uint16)
- *   fc2_scales  float  [T*k]    per-row FC2 input scale (1.0 for BF16 and MXFP8)
+ *   fc2_codes   uint8  [T*k, I] E4M3 (FP8, MXFP8), [T*k, I/2] E2M1 (MXFP4) or
+ *                               bf16 bits ([T*k, I] uint16)
+ *   fc2_scales  float  [T*k]    per-row FC2 input scale (1.0 for BF16 and MX formats)
  *   tok_bscales uint8  [T, 16*ceil(H/512)]   E8M0 block scales of the token
- *                                  codes (MXFP8 only), in matrix-core order:
+ *                                  codes (MXFP8, MXFP4), in matrix-core order:
  *                                  the scale of elements [32b, 32b + 32) of a
  *                                  row sits at byte 16*(b/16) + 4*(b%4) + (b/4)%4
- *   fc2_bscales uint8  [T*k, 16*ceil(I/512)] same for the FC2 codes (MXFP8 only)
+ *   fc2_bscales uint8  [T*k, 16*ceil(I/512)] same for the FC2 codes (MXFP8, MXFP4)
  *   y2          float  [T*k, H] GEMM2 output per expanded row
- *   num_tiles   int32  [1]      GEMM work-map length; tile_m rows per tile */
+ *   num_tiles   int32  [1]      GEMM work-map length; tile_m rows per tile
+ * gemm_cfg is the tile configuration the call uses (tuned or default, see
+ * moe_tune_set), max_tiles the bound on its work-map length. */
 typedef struct {
   size_t total;
   size_t ids, topk_w, chunk_counts, offsets, row_token, slot_row, tiles, num_tiles;
@@ -172,6 +180,46 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
 moe_status moe_run(const moe_dims* dims, const void* hidden, int64_t num_tokens,
                    const float* router_logits, const void* weights, const void* scales,
                    int32_t top_k, void* out, hipStream_t stream);
+
+/* Tile configurations of the grouped GEMMs.  A call picks one of
+ * MOE_NUM_GEMM_CFG configurations (0: 16-row tiles, 1: 48/64-row tiles, 2:
+ * 128/160-row tiles; the exact shapes depend on the formats and are reported
+ * by moe_workspace_layout as tile_m).  By default the choice follows the mean
+ * rows per expert (T*k/E: <= 16 -> 0, <= 48 -> 1, else 2).  A tuned choice
+ * overrides it for one layer shape (moe_dims), top_k and token bucket
+ * ceil(log2 num_tokens) for the rest of the process (flashinfer PR #3738,
+ * Implementation Notes: the MoE autotuner tunes both GEMMs over the tactics
+ * per shape, validates each tactic's results before timing it, and tunes on
+ * representative routing).  The workspace size never depends on the choice.
+ * All three functions are thread-safe; tuned choices are shared by all
+ * devices and streams of the process. */
+#define MOE_NUM_GEMM_CFG 3
+
+/* Sets (gemm_cfg in [0, MOE_NUM_GEMM_CFG)) or removes (gemm_cfg = -1) the
+ * tuned configuration of the bucket of num_tokens (>= 1).  Host only. */
+moe_status moe_tune_set(const moe_dims* dims, int64_t num_tokens, int32_t top_k,
+                        int32_t gemm_cfg);
+
+/* Forgets every tuned configuration.  Host only. */
+moe_status moe_tune_clear(void);
+
+/* Tunes the tile configuration on the caller's inputs (same arguments as
+ * moe_run_ws; num_tokens >= 1; use routing as skewed as the real workload).
+ * First runs the default configuration as the reference, then for every
+ * configuration: one run whose output must match the reference (relative L2
+ * <= 1e-3, same non-finite positions; the default itself is checked too), and
+ * only if it matches, `iters` (1..1000) timed runs between HIP events on
+ * `stream`.  Stores the fastest matching configuration for the bucket of
+ * num_tokens and returns it in *chosen; cfg_ms (optional, MOE_NUM_GEMM_CFG
+ * floats) receives each configuration's mean milliseconds per call, -1 for a
+ * rejected one.  Unlike the run calls it allocates (its own workspace and
+ * output, hipMalloc, freed before returning) and synchronises `stream`; the
+ * caller's out buffer is not touched.  MOE_ERR_INTERNAL if no configuration
+ * matches. */
+moe_status moe_autotune(const moe_dims* dims, const void* hidden, int64_t num_tokens,
+                        const float* router_logits, const void* weights, const void* scales,
+                        int32_t top_k, int32_t iters, int32_t* chosen, float* cfg_ms,
+                        hipStream_t stream);
 
 /* Stage timing.  With mode MOE_TRACE_ALL every moe_run_ws / moe_run call
  * records a HIP event on its stream before its first kernel and after each

@@ -15,16 +15,17 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_amd.so")
 
 W_MXFP4, W_INT4_G128 = 0, 1
-A_FP8_TOKEN, A_BF16, A_MXFP8 = 0, 1, 2
+A_FP8_TOKEN, A_BF16, A_MXFP8, A_MXFP4 = 0, 1, 2, 3
 WFMT = {"mxfp4": W_MXFP4, "int4": W_INT4_G128}
-AFMT = {"fp8": A_FP8_TOKEN, "bf16": A_BF16, "mxfp8": A_MXFP8}
+AFMT = {"fp8": A_FP8_TOKEN, "bf16": A_BF16, "mxfp8": A_MXFP8, "mxfp4": A_MXFP4}
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP", 5: "MOE_ERR_INTERNAL"}
 
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_weights_query", "moe_prepare_weights",
            "moe_unpack_weights", "moe_workspace_query", "moe_workspace_layout", "moe_run_ws",
-           "moe_run", "moe_trace_enable", "moe_trace_read")
+           "moe_run", "moe_tune_set", "moe_tune_clear", "moe_autotune", "moe_trace_enable",
+           "moe_trace_read")
 STAGES = ("route", "quant", "gemm1", "requant", "gemm2", "finalize")
 
 
@@ -70,6 +71,10 @@ def lib():
             "moe_workspace_layout": [DP, I64, I32, ctypes.POINTER(WsLayout)],
             "moe_run_ws": [DP, P, I64, P, P, P, I32, P, P, SZ, P],
             "moe_run": [DP, P, I64, P, P, P, I32, P, P],
+            "moe_tune_set": [DP, I64, I32, I32],
+            "moe_tune_clear": [],
+            "moe_autotune": [DP, P, I64, P, P, P, I32, I32, ctypes.POINTER(I32),
+                             ctypes.POINTER(ctypes.c_float), P],
             "moe_trace_enable": [I32],
             "moe_trace_read": [ctypes.POINTER(ctypes.c_float), I32, ctypes.POINTER(I32)],
         }
@@ -162,6 +167,31 @@ def run(d: LayerDims, hidden, logits, weights, scales, top_k: int, out, stream=N
     T = int(hidden.shape[0])
     _check(lib().moe_run(ctypes.byref(d.c()), _ptr(hidden), T, _ptr(logits), _ptr(weights),
                          _ptr(scales), top_k, _ptr(out), _stream(stream)))
+
+
+NUM_GEMM_CFG = 3
+
+
+def tune_set(d: LayerDims, num_tokens: int, top_k: int, gemm_cfg: int):
+    """Tile configuration for this shape and token bucket (-1 removes it)."""
+    _check(lib().moe_tune_set(ctypes.byref(d.c()), num_tokens, top_k, gemm_cfg))
+
+
+def tune_clear():
+    _check(lib().moe_tune_clear())
+
+
+def autotune(d: LayerDims, hidden, logits, weights, scales, top_k: int, iters: int = 5,
+             stream=None):
+    """Validates and times every tile configuration on these inputs, keeps the
+    fastest for the shape and token bucket; -> (chosen, [ms per call or -1])."""
+    T = int(hidden.shape[0])
+    chosen = ctypes.c_int32()
+    ms = (ctypes.c_float * NUM_GEMM_CFG)()
+    _check(lib().moe_autotune(ctypes.byref(d.c()), _ptr(hidden), T, _ptr(logits), _ptr(weights),
+                              _ptr(scales), top_k, iters, ctypes.byref(chosen), ms,
+                              _stream(stream)))
+    return chosen.value, [float(v) for v in ms]
 
 
 TRACE_OFF, TRACE_ALL, TRACE_GEMM1 = 0, 1, 2

@@ -15,6 +15,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <algorithm>
+#include <cmath>
 #include <map>
 #include <mutex>
 #include <string>
@@ -83,7 +84,8 @@ moe_status check_dims(const moe_dims* d) {
     return fail(MOE_ERR_INVALID_ARG, "inter %d must be a positive multiple of 128", d->inter);
   if (d->wfmt != MOE_W_MXFP4 && d->wfmt != MOE_W_INT4_G128)
     return fail(MOE_ERR_INVALID_ARG, "unknown weight format %d", d->wfmt);
-  if (d->afmt != MOE_A_FP8_TOKEN && d->afmt != MOE_A_BF16 && d->afmt != MOE_A_MXFP8)
+  if (d->afmt != MOE_A_FP8_TOKEN && d->afmt != MOE_A_BF16 && d->afmt != MOE_A_MXFP8 &&
+      d->afmt != MOE_A_MXFP4)
     return fail(MOE_ERR_INVALID_ARG, "unknown activation format %d", d->afmt);
   if (d->wfmt == MOE_W_INT4_G128 && d->afmt != MOE_A_FP8_TOKEN)
     return fail(MOE_ERR_UNSUPPORTED, "INT4 weights take per-token FP8 activations only");
@@ -115,6 +117,7 @@ Sizes sizes_of(const moe_dims* d) {
 int variant_of(const moe_dims* d) {
   if (d->wfmt == MOE_W_INT4_G128) return moe::kInt4Fp8;
   if (d->afmt == MOE_A_MXFP8) return moe::kMxfp4Mxfp8;
+  if (d->afmt == MOE_A_MXFP4) return moe::kMxfp4Mxfp4;
   return d->afmt == MOE_A_BF16 ? moe::kMxfp4Bf16 : moe::kMxfp4Fp8;
 }
 
@@ -126,9 +129,45 @@ int pick_cfg(int64_t rows, int32_t experts) {
   return 2;
 }
 
+// Tuned tile configurations (moe_tune_set / moe_autotune), per layer shape,
+// top-k and token-count bucket (ceil(log2 T)).  The flashinfer autotuner
+// (PR #3738, Implementation Notes) keeps its tuned tactics per problem shape
+// and token bucket in the same way.
+struct TuneKey {
+  int32_t e, h, i, wfmt, afmt, k, bucket;
+  bool operator<(const TuneKey& o) const {
+    const int32_t a[7] = {e, h, i, wfmt, afmt, k, bucket};
+    const int32_t b[7] = {o.e, o.h, o.i, o.wfmt, o.afmt, o.k, o.bucket};
+    return std::lexicographical_compare(a, a + 7, b, b + 7);
+  }
+};
+std::mutex g_tune_mu;
+std::map<TuneKey, int>& tune_table() {
+  static std::map<TuneKey, int> t;
+  return t;
+}
+TuneKey tune_key(const moe_dims* d, int64_t T, int32_t k) {
+  int32_t b = 0;
+  while (((int64_t)1 << b) < T) ++b;
+  return TuneKey{d->num_experts, d->hidden, d->inter, d->wfmt, d->afmt, k, b};
+}
+// Configuration a call uses: forced (>= 0), else tuned, else the heuristic.
+int cfg_for(const moe_dims* d, int64_t T, int32_t k, int force) {
+  if (force >= 0) return force;
+  {
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    auto it = tune_table().find(tune_key(d, T, k));
+    if (it != tune_table().end()) return it->second;
+  }
+  return pick_cfg(T * k, d->num_experts);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-moe_status layout_of(const moe_dims* d, int64_t T, int32_t k, moe_ws_layout* L) {
+// Workspace layout; force >= 0 selects the tile configuration.  The regions
+// do not depend on the configuration (the work map has room for 16-row
+// tiles), so tuning never changes the workspace size.
+moe_status layout_of(const moe_dims* d, int64_t T, int32_t k, moe_ws_layout* L, int force = -1) {
   MOE_TRY(check_dims(d));
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "num_tokens %lld < 0", (long long)T);
   if (k < 1 || k > moe::kMaxTopK || k > d->num_experts)
@@ -138,10 +177,11 @@ moe_status layout_of(const moe_dims* d, int64_t T, int32_t k, moe_ws_layout* L) 
   if (T > (int64_t)1 << 26 || rows >= ((int64_t)1 << 31))
     return fail(MOE_ERR_INVALID_ARG, "num_tokens %lld too large", (long long)T);
   const int64_t E = d->num_experts, H = d->hidden, I = d->inter;
-  const int cfg = pick_cfg(rows, d->num_experts);
+  const int cfg = cfg_for(d, T, k, force);
   const int tile_m = moe::gemm_cfg(cfg, variant_of(d)).bm();
   const int64_t nchunks = cdiv(T, moe::kRouteChunkTokens);
   const int64_t max_tiles = cdiv(rows, tile_m) + std::min<int64_t>(E, rows);
+  const int64_t map_room = cdiv(rows, 16) + std::min<int64_t>(E, rows);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -155,13 +195,15 @@ moe_status layout_of(const moe_dims* d, int64_t T, int32_t k, moe_ws_layout* L) 
   L->offsets = take((E + 1) * 4);
   L->row_token = take(rows * 4);
   L->slot_row = take(rows * 4);
-  L->tiles = take(max_tiles * sizeof(moe::Tile));
+  L->tiles = take(map_room * sizeof(moe::Tile));
   L->num_tiles = take(4);
-  const bool e4m3 = d->afmt != MOE_A_BF16, mx = d->afmt == MOE_A_MXFP8;
-  L->tok_codes = take(e4m3 ? T * H : 0);
-  L->tok_scales = take(e4m3 ? T * 4 : 0);
+  const bool e2m1 = d->afmt == MOE_A_MXFP4;
+  const bool e4m3 = d->afmt == MOE_A_FP8_TOKEN || d->afmt == MOE_A_MXFP8;
+  const bool mx = d->afmt == MOE_A_MXFP8 || e2m1;
+  L->tok_codes = take(e4m3 ? T * H : e2m1 ? T * H / 2 : 0);
+  L->tok_scales = take(e4m3 || e2m1 ? T * 4 : 0);
   L->h = take(rows * I * 4);
-  L->fc2_codes = take(rows * I * (e4m3 ? 1 : 2));
+  L->fc2_codes = take(e4m3 ? rows * I : e2m1 ? rows * I / 2 : rows * I * 2);
   L->fc2_scales = take(rows * 4);
   L->y2 = take(rows * H * 4);
   L->tok_bscales = take(mx ? T * moe::mx_scale_row_bytes(H) : 0);
@@ -362,12 +404,17 @@ moe_status moe_workspace_layout(const moe_dims* dims, int64_t num_tokens, int32_
   return ok();
 }
 
-moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_tokens,
-                      const float* router_logits, const void* weights, const void* scales,
-                      int32_t top_k, void* out, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The layer with tile configuration `force` (< 0: tuned or heuristic).
+moe_status run_checked(const moe_dims* dims, const void* hidden, int64_t num_tokens,
+                       const float* router_logits, const void* weights, const void* scales,
+                       int32_t top_k, void* out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, int force) {
   moe_ws_layout L;
-  MOE_TRY(layout_of(dims, num_tokens, top_k, &L));
+  MOE_TRY(layout_of(dims, num_tokens, top_k, &L, force));
   if (num_tokens == 0) return ok();
   if (!hidden || !router_logits || !weights || !scales || !out || !workspace)
     return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
@@ -384,7 +431,9 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
   const Sizes s = sizes_of(dims);
   const int64_t T = num_tokens, rows = T * top_k;
   const int32_t E = dims->num_experts, H = dims->hidden, I = dims->inter;
-  const bool fp8 = dims->afmt == MOE_A_FP8_TOKEN, mx = dims->afmt == MOE_A_MXFP8;
+  const bool fp8 = dims->afmt == MOE_A_FP8_TOKEN, e2m1 = dims->afmt == MOE_A_MXFP4;
+  const bool mx = dims->afmt == MOE_A_MXFP8 || e2m1;
+  const int mx_mode = e2m1 ? moe::kQuantMxfp4 : moe::kQuantMxfp8;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
 
   moe::RouteParams rp;
@@ -414,13 +463,13 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
     float* sc = reinterpret_cast<float*>(ws + L.tok_scales);
     uint8_t* bsc = mx ? ws + L.tok_bscales : nullptr;
     MOE_TRY(hip_check(moe::launch_quant_tokens(static_cast<const uint16_t*>(hidden), T, H,
-                                               mx ? moe::kQuantMxfp8 : moe::kQuantFp8Row,
+                                               mx ? mx_mode : moe::kQuantFp8Row,
                                                codes, sc, bsc, stream),
                       "quantize tokens", stream));
     if (fp8) tok_scales = sc;
     tok_bscales = bsc;
     a1 = codes;
-    a1_stride = H;
+    a1_stride = e2m1 ? H / 2 : H;
   }
   trace_mark(tc, 2, stream);
 
@@ -455,7 +504,7 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
   uint8_t* q2 = ws + L.fc2_codes;
   float* s2 = reinterpret_cast<float*>(ws + L.fc2_scales);
   uint8_t* b2 = mx ? ws + L.fc2_bscales : nullptr;
-  const int rq_mode = fp8 ? moe::kQuantFp8Row : (mx ? moe::kQuantMxfp8 : moe::kQuantBf16);
+  const int rq_mode = fp8 ? moe::kQuantFp8Row : (mx ? mx_mode : moe::kQuantBf16);
   MOE_TRY(hip_check(moe::launch_requant(h, rows, I, rq_mode, q2, s2, b2, stream),
                     "fc2 requant", stream));
   trace_mark(tc, 4, stream);
@@ -463,7 +512,7 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
   float* y2 = reinterpret_cast<float*>(ws + L.y2);
   moe::GemmParams g2;
   g2.a = q2;
-  g2.a_stride = (int64_t)I * (fp8 || mx ? 1 : 2);
+  g2.a_stride = e2m1 ? (int64_t)I / 2 : (int64_t)I * (fp8 || mx ? 1 : 2);
   g2.row_token = nullptr;
   g2.row_scale = fp8 ? s2 : nullptr;
   g2.a_scale = b2;
@@ -487,6 +536,142 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
                                          static_cast<uint16_t*>(out), stream),
                     "finalize", stream));
   trace_mark(tc, 6, stream);
+  return ok();
+}
+
+// Host copy of a bf16 device buffer as float.
+moe_status fetch_bf16(const void* dev, size_t n, std::vector<float>* outv) {
+  std::vector<uint16_t> bits(n);
+  hipError_t e = hipMemcpy(bits.data(), dev, n * 2, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipMemcpy: %s", hipGetErrorString(e));
+  outv->resize(n);
+  for (size_t i = 0; i < n; ++i) {
+    const uint32_t u = (uint32_t)bits[i] << 16;
+    std::memcpy(&(*outv)[i], &u, 4);
+  }
+  return MOE_OK;
+}
+
+// Device buffers and events of one moe_autotune call, released on every path.
+struct TuneScratch {
+  void* ws = nullptr;
+  void* out = nullptr;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  ~TuneScratch() {
+    if (ws) (void)hipFree(ws);
+    if (out) (void)hipFree(out);
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_tokens,
+                      const float* router_logits, const void* weights, const void* scales,
+                      int32_t top_k, void* out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  return run_checked(dims, hidden, num_tokens, router_logits, weights, scales, top_k, out,
+                     workspace, workspace_bytes, stream, -1);
+}
+
+moe_status moe_tune_set(const moe_dims* dims, int64_t num_tokens, int32_t top_k,
+                        int32_t gemm_cfg) {
+  moe_ws_layout L;
+  MOE_TRY(layout_of(dims, num_tokens, top_k, &L));
+  if (num_tokens < 1) return fail(MOE_ERR_INVALID_ARG, "num_tokens must be >= 1");
+  if (gemm_cfg < -1 || gemm_cfg >= moe::kNumGemmCfg)
+    return fail(MOE_ERR_INVALID_ARG, "gemm_cfg %d outside [-1, %d)", gemm_cfg, moe::kNumGemmCfg);
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  const TuneKey key = tune_key(dims, num_tokens, top_k);
+  if (gemm_cfg < 0) tune_table().erase(key);
+  else tune_table()[key] = gemm_cfg;
+  return ok();
+}
+
+moe_status moe_tune_clear(void) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  tune_table().clear();
+  return ok();
+}
+
+moe_status moe_autotune(const moe_dims* dims, const void* hidden, int64_t num_tokens,
+                        const float* router_logits, const void* weights, const void* scales,
+                        int32_t top_k, int32_t iters, int32_t* chosen, float* cfg_ms,
+                        hipStream_t stream) {
+  moe_ws_layout L;
+  MOE_TRY(layout_of(dims, num_tokens, top_k, &L));
+  if (num_tokens < 1) return fail(MOE_ERR_INVALID_ARG, "num_tokens must be >= 1");
+  if (!chosen) return fail(MOE_ERR_INVALID_ARG, "null output pointer");
+  if (iters < 1 || iters > 1000) return fail(MOE_ERR_INVALID_ARG, "iters %d outside [1, 1000]", iters);
+  MOE_TRY(check_device());
+  const int64_t T = num_tokens;
+  const size_t n_out = (size_t)T * dims->hidden;
+  TuneScratch sc;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e == hipSuccess) e = hipMalloc(&sc.ws, L.total);
+  if (e == hipSuccess) e = hipMalloc(&sc.out, n_out * 2);
+  if (e == hipSuccess) e = hipEventCreate(&sc.ev[0]);
+  if (e == hipSuccess) e = hipEventCreate(&sc.ev[1]);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "autotune setup: %s", hipGetErrorString(e));
+
+  // reference: the heuristic configuration (the one the parity tests pin)
+  const int ref_cfg = pick_cfg(T * top_k, dims->num_experts);
+  std::vector<float> ref, got;
+  MOE_TRY(run_checked(dims, hidden, T, router_logits, weights, scales, top_k, sc.out, sc.ws,
+                      L.total, stream, ref_cfg));
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "autotune: %s", hipGetErrorString(e));
+  MOE_TRY(fetch_bf16(sc.out, n_out, &ref));
+  double ref2 = 0.0;
+  for (float v : ref) ref2 += (double)v * v;
+
+  int best = -1;
+  float best_ms = 0.0f;
+  for (int c = 0; c < moe::kNumGemmCfg; ++c) {
+    float ms = -1.0f;
+    // correctness first: one run against the reference output (relative L2
+    // below 1e-3, NaN-free); a failing configuration is never timed
+    MOE_TRY(run_checked(dims, hidden, T, router_logits, weights, scales, top_k, sc.out, sc.ws,
+                        L.total, stream, c));
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "autotune: %s", hipGetErrorString(e));
+    MOE_TRY(fetch_bf16(sc.out, n_out, &got));
+    double d2 = 0.0;
+    bool finite = true;
+    for (size_t i = 0; i < n_out; ++i) {
+      const double d = (double)got[i] - (double)ref[i];
+      finite = finite && std::isfinite(got[i]) == std::isfinite(ref[i]);
+      if (std::isfinite(d)) d2 += d * d;
+    }
+    const bool valid = finite && d2 <= 1e-6 * ref2;
+    if (valid) {
+      e = hipEventRecord(sc.ev[0], stream);
+      for (int it = 0; it < iters && e == hipSuccess; ++it) {
+        MOE_TRY(run_checked(dims, hidden, T, router_logits, weights, scales, top_k, sc.out,
+                            sc.ws, L.total, stream, c));
+      }
+      if (e == hipSuccess) e = hipEventRecord(sc.ev[1], stream);
+      if (e == hipSuccess) e = hipEventSynchronize(sc.ev[1]);
+      float total = 0.0f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&total, sc.ev[0], sc.ev[1]);
+      if (e != hipSuccess) return fail(MOE_ERR_HIP, "autotune timing: %s", hipGetErrorString(e));
+      ms = total / (float)iters;
+      if (best < 0 || ms < best_ms) {
+        best = c;
+        best_ms = ms;
+      }
+    }
+    if (cfg_ms) cfg_ms[c] = ms;
+  }
+  if (best < 0) return fail(MOE_ERR_INTERNAL, "no tile configuration matched the reference");
+  {
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    tune_table()[tune_key(dims, T, top_k)] = best;
+  }
+  *chosen = best;
   return ok();
 }
 

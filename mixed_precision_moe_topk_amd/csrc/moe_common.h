@@ -21,12 +21,18 @@ enum Variant : int {
   kMxfp4Bf16 = 1,  // E2M1 weights (E8M0 / 32) x bf16 activations
   kInt4Fp8 = 2,    // INT4 weights (fp32 / 128) x per-token E4M3 activations
   kMxfp4Mxfp8 = 3, // E2M1 weights (E8M0 / 32) x E4M3 activations (E8M0 / 32)
+  kMxfp4Mxfp4 = 4, // E2M1 weights (E8M0 / 32) x E2M1 activations (E8M0 / 32), W4A4
 };
 
 // Weights and activations both carry E8M0 block scales, applied by the MFMA.
-constexpr bool a_blockscaled(int v) { return v == kMxfp4Mxfp8; }
-// E2M1 weights with E4M3 activations: the block-scaled FP8 x FP4 MFMA.
-constexpr bool fp8_x_fp4(int v) { return v == kMxfp4Fp8 || v == kMxfp4Mxfp8; }
+constexpr bool a_blockscaled(int v) { return v == kMxfp4Mxfp8 || v == kMxfp4Mxfp4; }
+// E2M1 weights on the block-scaled MFMA (E4M3 or E2M1 activations).
+constexpr bool scaled_fp4(int v) { return v == kMxfp4Fp8 || v == kMxfp4Mxfp8 || v == kMxfp4Mxfp4; }
+// E2M1 activations: the A operand is 4 registers of 32 consecutive k per lane
+// (64 bytes per row and 128-wide K step) and the MFMA runs at the FP4 rate.
+constexpr bool a_fp4(int v) { return v == kMxfp4Mxfp4; }
+// MFMA format code of the A operand (0 E4M3, 4 E2M1).
+constexpr int a_fmt(int v) { return a_fp4(v) ? 4 : 0; }
 
 // Work-map entry of the grouped GEMMs: rows [row0, row0 + nrows) of expert
 // `expert` (entries are grouped by expert, in expert order).
@@ -65,6 +71,13 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 // Round a finite float to the nearest OCP E4M3 ("FN") code: ties to even
 // mantissa, magnitudes above 448 saturate to 448, the sign is kept when the
 // magnitude rounds to zero.  Integer bit manipulation on the float32 pattern.
+// Nearest E2M1 magnitude code (0, 0.5, 1, 1.5, 2, 3, 4, 6 -> 0..7) of a
+// non-negative value, ties to the even code, saturating at 6.
+__device__ __forceinline__ uint32_t e2m1_magnitude_code(float v_abs) {
+  return (v_abs > 0.25f) + (v_abs >= 0.75f) + (v_abs > 1.25f) + (v_abs >= 1.75f) +
+         (v_abs > 2.5f) + (v_abs >= 3.5f) + (v_abs > 5.0f);
+}
+
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
   const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
   const float a = fminf(fabsf(v), 448.0f);
@@ -167,10 +180,10 @@ __host__ __device__ constexpr int64_t mx_scale_offset(int64_t kb) {  // kb = col
 // ---------------------------------------------------------------- launchers
 hipError_t launch_route(const RouteParams& p, hipStream_t st);
 // Activation quantisation modes of the token and FC2-input quantisers.
-enum QuantMode : int { kQuantFp8Row = 0, kQuantBf16 = 1, kQuantMxfp8 = 2 };
-// FP8 rows: codes + one float scale per row; MXFP8: codes + E8M0 per 32
-// (bscales [rows][mx_scale_row_bytes(C)] in MFMA scale order, row scales
-// written as 1.0); BF16: bits, scale 1.
+enum QuantMode : int { kQuantFp8Row = 0, kQuantBf16 = 1, kQuantMxfp8 = 2, kQuantMxfp4 = 3 };
+// FP8 rows: codes + one float scale per row; MXFP8 / MXFP4: E4M3 codes [C] /
+// packed E2M1 codes [C/2] + E8M0 per 32 (bscales [rows][mx_scale_row_bytes(C)]
+// in MFMA scale order, row scales written as 1.0); BF16: bits, scale 1.
 hipError_t launch_quant_tokens(const uint16_t* x, int64_t T, int32_t H, int mode,
                                uint8_t* codes, float* scales, uint8_t* bscales, hipStream_t st);
 hipError_t launch_requant(const float* h, int64_t rows, int32_t I, int mode, uint8_t* codes,
@@ -208,6 +221,7 @@ inline GemmCfg gemm_cfg(int i, int variant) {
     default:
       return variant == kMxfp4Bf16 ? GemmCfg{4, 2, 4, 4}    // 128 x 128
              : variant == kMxfp4Mxfp8 ? GemmCfg{8, 2, 4, 8}  // 128 x 512
+             : variant == kMxfp4Mxfp4 ? GemmCfg{8, 2, 5, 8}  // 160 x 512
              : variant == kMxfp4Fp8 ? GemmCfg{8, 2, 5, 8}    // 160 x 512
                                   : GemmCfg{8, 2, 4, 4};   // 128 x 256
   }

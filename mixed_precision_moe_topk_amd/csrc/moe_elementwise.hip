@@ -143,25 +143,30 @@ __global__ __launch_bounds__(256) void k_requant(const float* __restrict__ h, in
   if (threadIdx.x == 0) scales[r] = s;
 }
 
-// ---------------------------------------------------------------- MXFP8
-// OCP MX conversion with E4M3 elements (emax 8): per 32 consecutive elements
-// X = floor(log2 amax) - 8 (clamped to [-127, 127]; amax = 0 -> code 127),
-// elements E4M3(v * 2^-X) rounded to nearest even and saturated at 448.
-// v * 2^-X is exact in float32 unless the product is below 2^-126, where the
-// E4M3 code is +-0 either way.  (MXFP8 inputs of flashinfer PR #4793, "Unify
-// MoE CuTe DSL dispatch to be dtype agnostic", and PR #3614's MXFP8xMXFP8.)
-__device__ __forceinline__ int mx_e4m3_exponent(float amax) {
+// ---------------------------------------------------------------- MXFP8 / MXFP4
+// OCP MX conversion: per 32 consecutive elements X = floor(log2 amax) - emax
+// (emax 8 for E4M3 elements, 2 for E2M1; clamped to [-127, 127]; amax = 0 ->
+// X = 0, code 127), elements E4M3 / E2M1 of v * 2^-X rounded to nearest even
+// and saturated (448 / 6).  v * 2^-X is exact in float32 unless the product
+// is below 2^-126, where the code is +-0 either way.  (MXFP8 inputs of
+// flashinfer PR #4793, "Unify MoE CuTe DSL dispatch to be dtype agnostic",
+// and PR #3614's MXFP8xMXFP8; the MXFP4 activation pack of PR #4793's w4a4
+// mode, quantised like the weights.)
+template <int EMAX>
+__device__ __forceinline__ int mx_exponent(float amax) {
   if (!(amax > 0.0f)) return 0;
   const uint32_t b = __float_as_uint(amax);
   const int e = (int)((b >> 23) & 0xFFu);
   const int fl = e ? e - 127 : (31 - __clz(b & 0x7FFFFFu)) - 149;  // floor(log2 amax)
-  return min(max(fl - 8, -127), 127);
+  return min(max(fl - EMAX, -127), 127);
 }
 
 // Eight consecutive elements per thread, four threads (consecutive lanes) per
 // 32-element block.  `valid`: the group's block lies inside the row (rows are
 // a multiple of 32 long, so a group is wholly inside or outside).  Returns
-// the eight codes; *code = the block's E8M0 code.
+// the eight codes (E4M3: 8 bytes; E2M1: one dword, element i in bits 4i..4i+3,
+// i.e. element 2j in the low nibble of byte j); *code = the block's E8M0 code.
+template <bool E2M1>
 __device__ __forceinline__ uint2 mx_quant8(const float (&v)[8], bool valid, uint32_t* code) {
   float amax = 0.0f;
 #pragma unroll
@@ -169,20 +174,26 @@ __device__ __forceinline__ uint2 mx_quant8(const float (&v)[8], bool valid, uint
   if (!valid) amax = 0.0f;
   amax = fmaxf(amax, __shfl_xor(amax, 1));
   amax = fmaxf(amax, __shfl_xor(amax, 2));
-  const int x = mx_e4m3_exponent(amax);
+  const int x = mx_exponent<E2M1 ? 2 : 8>(amax);
   *code = (uint32_t)(x + 127);
   const float inv = __uint_as_float((uint32_t)(127 - x) << 23);  // 2^-X, a normal float
   uint32_t c[2] = {0, 0};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i / 4] |= e4m3_encode(v[i] * inv) << (8 * (i & 3));
+  for (int i = 0; i < 8; ++i) {
+    if (E2M1)
+      c[0] |= (e2m1_magnitude_code(fabsf(v[i]) * inv) | ((__float_as_uint(v[i]) >> 31) << 3))
+              << (4 * i);
+    else
+      c[i / 4] |= e4m3_encode(v[i] * inv) << (8 * (i & 3));
+  }
   return make_uint2(c[0], c[1]);
 }
 
 // One block (256 threads) per row of C elements (C % 32 == 0), 2048 elements
-// per pass: bf16 (SRC_BF16) or float32 input -> E4M3 codes [C] + E8M0 codes
-// in the block-scaled MFMA's scale order (mx_scale_offset); the row's float
-// scale is written as 1.0.
-template <bool SRC_BF16>
+// per pass: bf16 (SRC_BF16) or float32 input -> E4M3 codes [C] (E2M1: packed
+// codes [C/2]) + E8M0 codes in the block-scaled MFMA's scale order
+// (mx_scale_offset); the row's float scale is written as 1.0.
+template <bool SRC_BF16, bool E2M1>
 __global__ __launch_bounds__(256) void k_quant_mx(const void* __restrict__ src, int32_t C,
                                                   uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ bscales,
@@ -208,9 +219,10 @@ __global__ __launch_bounds__(256) void k_quant_mx(const void* __restrict__ src, 
       v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
     uint32_t code;
-    const uint2 q = mx_quant8(v, valid, &code);
+    const uint2 q = mx_quant8<E2M1>(v, valid, &code);
     if (valid) {
-      reinterpret_cast<uint2*>(codes + r * C)[i] = q;
+      if (E2M1) reinterpret_cast<uint32_t*>(codes + r * (C / 2))[i] = q.x;
+      else reinterpret_cast<uint2*>(codes + r * C)[i] = q;
       if ((i & 3) == 0) bscales[r * mx_scale_row_bytes(C) + mx_scale_offset(i / 4)] = (uint8_t)code;
     }
   }
@@ -265,7 +277,8 @@ __global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ y2,
 hipError_t launch_quant_tokens(const uint16_t* x, int64_t T, int32_t H, int mode,
                                uint8_t* codes, float* scales, uint8_t* bscales, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  if (mode == kQuantMxfp8) k_quant_mx<true><<<(unsigned)T, 256, 0, st>>>(x, H, codes, bscales, scales);
+  if (mode == kQuantMxfp8) k_quant_mx<true, false><<<(unsigned)T, 256, 0, st>>>(x, H, codes, bscales, scales);
+  else if (mode == kQuantMxfp4) k_quant_mx<true, true><<<(unsigned)T, 256, 0, st>>>(x, H, codes, bscales, scales);
   else k_quant_tokens<<<(unsigned)T, 256, 0, st>>>(x, H, codes, scales);
   return hipGetLastError();
 }
@@ -274,7 +287,9 @@ hipError_t launch_requant(const float* h, int64_t rows, int32_t I, int mode, uin
                           float* scales, uint8_t* bscales, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   if (mode == kQuantMxfp8)
-    k_quant_mx<false><<<(unsigned)rows, 256, 0, st>>>(h, I, codes, bscales, scales);
+    k_quant_mx<false, false><<<(unsigned)rows, 256, 0, st>>>(h, I, codes, bscales, scales);
+  else if (mode == kQuantMxfp4)
+    k_quant_mx<false, true><<<(unsigned)rows, 256, 0, st>>>(h, I, codes, bscales, scales);
   else
     k_requant<<<(unsigned)rows, 256, 0, st>>>(h, I, mode == kQuantBf16 ? 1 : 0, codes, scales);
   return hipGetLastError();

@@ -13,6 +13,8 @@
 //                   in the epilogue.
 //   * MXFP4 x MXFP8: the same MFMA with the activations' E8M0 block scales as
 //                   its A scale operand (no epilogue scale).
+//   * MXFP4 x MXFP4 (W4A4): the same MFMA with E2M1 activations (A format
+//                   code 4, four operand registers, twice the FP8 rate).
 //   * MXFP4 x BF16: weights expanded to bf16 in registers with the E8M0 scale
 //                   folded in (exact), then bf16 MFMA 16x16x32.
 //   * INT4 x FP8  : INT4 codes mapped to E4M3 (exact) in registers, one FP8
@@ -46,6 +48,10 @@ struct Frag<kMxfp4Fp8> {
 template <>
 struct Frag<kMxfp4Mxfp8> {
   static constexpr int kA = 2;
+};
+template <>
+struct Frag<kMxfp4Mxfp4> {
+  static constexpr int kA = 1;
 };
 template <>
 struct Frag<kInt4Fp8> {

@@ -14,6 +14,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int NA = Frag<V>::kA;
   constexpr bool MXA = a_blockscaled(V);
+  constexpr int AF = a_fmt(V);
   static_assert(!FC1 || WN % 2 == 0, "FC1 pairs gate/up tiles");
   Tile tile;
   int nt;
@@ -43,7 +44,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     const int r = min(row_base + 16 * i + (lane & 15), row_end - 1);
     const int64_t src = FC1 ? (int64_t)p.row_token[r] : (int64_t)r;
     int64_t off;
-    if (fp8_x_fp4(V)) off = 16 * (lane >> 4);
+    if (scaled_fp4(V)) off = 16 * (lane >> 4);  // E4M3: bytes 16g.. (+64); E2M1: k 32g..
     else if (V == kInt4Fp8) off = 32 * (lane >> 4);
     else off = 64 * (lane >> 4);  // bf16: 32 elements * 2 bytes
     arow[i] = p.a + src * p.a_stride + off;
@@ -68,7 +69,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       if (i < nvalid) {
-        if (fp8_x_fp4(V)) {
+        if (a_fp4(V)) {
+          a[i][0] = *reinterpret_cast<const uint4*>(arow[i] + ks * (kKStep / 2));
+          as[i] = *reinterpret_cast<const uint32_t*>(asrow[i] + 16 * (ks >> 2));
+        } else if (scaled_fp4(V)) {
           a[i][0] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep);
           a[i][1] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep + 64);
           if (a_blockscaled(V))
@@ -97,23 +101,23 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
 
   auto compute = [&](int ks, const uint4 (&a)[WM][NA], const uint4 (&b)[WN],
                      const uint32_t (&sc)[WN], const uint32_t (&as)[WM]) {
-    if (fp8_x_fp4(V)) {
+    if (scaled_fp4(V)) {
       v8i bop[WN];
 #pragma unroll
       for (int j = 0; j < WN; ++j) bop[j] = fp4_operand(b[j]);
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
         if (i < nvalid) {
-          const v8i aop = as_v8i(a[i][0], a[i][1]);
+          const v8i aop = a_fp4(V) ? fp4_operand(a[i][0]) : as_v8i(a[i][0], a[i][NA - 1]);
           const int sa = MXA ? (int)as[i] : 127;
 #pragma unroll
           for (int j = 0; j < WN; ++j) {
             if (j >= jvalid) continue;
             switch (ks & 3) {
-              case 0: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, sa, 0, (int)sc[j]); break;
-              case 1: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, MXA ? 1 : 0, sa, 1, (int)sc[j]); break;
-              case 2: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, MXA ? 2 : 0, sa, 2, (int)sc[j]); break;
-              default: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], 0, 4, MXA ? 3 : 0, sa, 3, (int)sc[j]); break;
+              case 0: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], AF, 4, 0, sa, 0, (int)sc[j]); break;
+              case 1: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], AF, 4, MXA ? 1 : 0, sa, 1, (int)sc[j]); break;
+              case 2: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], AF, 4, MXA ? 2 : 0, sa, 2, (int)sc[j]); break;
+              default: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], AF, 4, MXA ? 3 : 0, sa, 3, (int)sc[j]); break;
             }
           }
         }
@@ -193,6 +197,8 @@ hipError_t launch_gemm_direct(int variant, bool fc1, int cfg, const GemmParams& 
                                 : launch_v<kMxfp4Bf16, false>(cfg, p, blocks, st);
     case kMxfp4Mxfp8: return fc1 ? launch_v<kMxfp4Mxfp8, true>(cfg, p, blocks, st)
                                  : launch_v<kMxfp4Mxfp8, false>(cfg, p, blocks, st);
+    case kMxfp4Mxfp4: return fc1 ? launch_v<kMxfp4Mxfp4, true>(cfg, p, blocks, st)
+                                 : launch_v<kMxfp4Mxfp4, false>(cfg, p, blocks, st);
     default: return fc1 ? launch_v<kInt4Fp8, true>(cfg, p, blocks, st)
                         : launch_v<kInt4Fp8, false>(cfg, p, blocks, st);
   }

@@ -53,17 +53,21 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
   constexpr int NB = (PB == 1) ? 2 : 4;  // weight register sets (prefetch distance PB)
   constexpr int AS = (AD == 2) ? 2 : 4;  // A staging register sets (prefetch distance AD)
 
-  static_assert(fp8_x_fp4(V) || V == kInt4Fp8, "E4M3 activations only");
+  static_assert(scaled_fp4(V) || V == kInt4Fp8, "E4M3 or E2M1 activations only");
   static_assert(!FC1 || WN % 2 == 0, "FC1 pairs gate/up tiles");
   constexpr int NT = kWave * NW;           // threads per block
   constexpr int WAVES_N = NW / WAVES_M;
   constexpr int BM = 16 * WM * WAVES_M;
   static_assert(BM % 32 == 0, "BM must be a multiple of 32");
-  static_assert((BM * 8) % NT == 0, "A stage must split evenly over the threads");
-  constexpr int ABUF = BM * kKStep;        // bytes of one A stage
-  constexpr int NCH = BM * 8 / NT;         // 16-byte chunks per thread per stage
-  constexpr bool MX = fp8_x_fp4(V);
+  constexpr bool MX = scaled_fp4(V);
   constexpr bool MXA = a_blockscaled(V);
+  constexpr bool A4 = a_fp4(V);
+  constexpr int AF = a_fmt(V);             // MFMA format code of A (a constant expression)
+  constexpr int CPR = A4 ? 4 : 8;          // 16-byte chunks per A row and K step
+  constexpr int NF = A4 ? 1 : 2;           // 1 KB operand fragments per 16 rows
+  static_assert((BM * CPR) % NT == 0, "A stage must split evenly over the threads");
+  constexpr int ABUF = BM * 16 * CPR;      // bytes of one A stage
+  constexpr int NCH = BM * CPR / NT;       // 16-byte chunks per thread per stage
 
   // wave-uniform values are made scalar so that branches on them are scalar
   // branches (exec-masked branches make the compiler drain every outstanding
@@ -88,21 +92,23 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
   const int jvalid = cols ? WN : 0;
 
   // this thread's A chunks: tile row r, 16-byte column chunk c; source pointer
-  // and LDS destination (fragment (r/16, h), lane (r%16) + 16*g)
+  // and LDS destination (fragment (r/16, h), lane (r%16) + 16*g; E2M1 rows
+  // have one fragment per 16 rows, chunk c = the 32 elements of lane group c)
   const uint8_t* asrc[NCH];
   int adst[NCH];
 #pragma unroll
   for (int u = 0; u < NCH; ++u) {
     const int q = threadIdx.x + NT * u;
-    const int r = q >> 3, c = q & 7;
+    const int r = q / CPR, c = q % CPR;
     const int rr = min(tile.row0 + r, row_end - 1);
     const int64_t src = FC1 ? (int64_t)p.row_token[rr] : (int64_t)rr;
     asrc[u] = p.a + src * p.a_stride + 16 * c;
     int g, h;
-    if (MX) { g = c & 3; h = c >> 2; }               // k = 64h + 16g + [0,16)
+    if (A4) { g = c; h = 0; }                        // k = 32g + [0,32)
+    else if (MX) { g = c & 3; h = c >> 2; }          // k = 64h + 16g + [0,16)
     else { g = c >> 1; h = c & 1; }                  // k = 32g + 16h + [0,16)
     const int rho = r & 15;
-    adst[u] = ((r >> 4) * 2 + h) * 1024 + (16 * g + (rho ^ ((2 * g + h) | ((rho & 1) << 3)))) * 16;
+    adst[u] = ((r >> 4) * NF + h) * 1024 + (16 * g + (rho ^ ((2 * g + h) | ((rho & 1) << 3)))) * 16;
   }
   // this lane's read offsets inside a fragment of half h = 0 / 1
   const int rho_l = lane & 15, g_l = lane >> 4;
@@ -134,7 +140,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
 
   auto load_a = [&](int ks, v4u (&dst)[NCH]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < NCH; ++u) dst[u] = *reinterpret_cast<const v4u*>(asrc[u] + ks * kKStep);
+    for (int u = 0; u < NCH; ++u) dst[u] = *reinterpret_cast<const v4u*>(asrc[u] + ks * (16 * CPR));
   };
   auto store_a = [&](int buf, const v4u (&src)[NCH]) __attribute__((always_inline)) {
 #pragma unroll
@@ -190,7 +196,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
     // writes + barrier) so the wait counts refer to the intended loads
     __builtin_amdgcn_sched_barrier(0);
 #endif
-    const uint8_t* abuf = lds + (S & 1) * ABUF + (WM * wm) * 2048;
+    const uint8_t* abuf = lds + (S & 1) * ABUF + (WM * wm) * (NF * 1024);
     v8i bop[WN];
 #pragma unroll
     for (int j = 0; j < WN; ++j)
@@ -198,14 +204,19 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       if (FULL || (cols && i < nvalid)) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(abuf + (2 * i) * 1024 + rd0);
-        const uint4 hi = *reinterpret_cast<const uint4*>(abuf + (2 * i) * 1024 + rd1);
-        const v8i aop = as_v8i(lo, hi);
+        const uint4 lo = *reinterpret_cast<const uint4*>(abuf + (NF * i) * 1024 + rd0);
+        v8i aop;
+        if constexpr (A4) {
+          aop = fp4_operand(lo);
+        } else {
+          const uint4 hi = *reinterpret_cast<const uint4*>(abuf + (NF * i) * 1024 + rd1);
+          aop = as_v8i(lo, hi);
+        }
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
           if (MX) {
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                aop, bop[j], acc[i][j], 0, 4, MXA ? S : 0, MXA ? (int)ax[i] : 127, S, (int)sx[j]);
+                aop, bop[j], acc[i][j], AF, 4, MXA ? S : 0, MXA ? (int)ax[i] : 127, S, (int)sx[j]);
           } else {
             const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 aop, bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
@@ -219,7 +230,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
 #if MOE_INTERLEAVE
     // issue order inside the step: the wave's global loads and LDS reads are
     // spread between its MFMAs so they issue while the matrix pipe is busy
-    if (FULL) interleave_schedule<WM * WN, (MX ? (LOAD_SX ? 2 : 1) : 2) * WN + NCH + (LOAD_SX && MXA ? WM : 0), 2 * WM>();
+    if (FULL) interleave_schedule<WM * WN, (MX ? (LOAD_SX ? 2 : 1) : 2) * WN + NCH + (LOAD_SX && MXA ? WM : 0), NF * WM>();
 #endif
     __builtin_amdgcn_sched_barrier(0);
     // A of step ks+1 (a harmless copy of the last step once past the end)
@@ -528,13 +539,14 @@ constexpr int kBPW = kBNB / kNW;        // weight blocks loaded per wave
 static_assert(kBPW * kNW == kBNB, "weight blocks per wave");
 constexpr int kBBuf = kBNB * 1024, kSxSlot = kBNB * 256;
 // LDS map of a tile whose waves own WM 16-row subtiles each (MXA: with the
-// activation-scale slots)
-template <int WM, bool MXA>
+// activation-scale slots; A4: E2M1 activations, 64 bytes per row and step)
+template <int WM, bool MXA, bool A4>
 struct Map {
   static constexpr int kBM = 2 * 16 * WM;   // tile rows
   static constexpr int kRG = kBM / 16;      // 16-row groups (wave w loads w and w + 8)
   static_assert(kRG >= kNW && kRG <= 2 * kNW, "row groups per wave");
-  static constexpr int kABuf = kBM * kKStep;
+  static constexpr int kNF = A4 ? 1 : 2;    // 1 KB operand fragments per 16 rows
+  static constexpr int kABuf = kBM * 16 * 4 * kNF;
   static constexpr int kAOff = 0, kBOff = 2 * kABuf, kSOff = kBOff + 3 * kBBuf;
   static constexpr int kAsDma = (kBM + 63) / 64;  // activation-scale loads per group (waves 0..)
   static constexpr int kAsSlot = kAsDma * 1024, kAsOff = kSOff + 2 * kSxSlot;
@@ -568,10 +580,13 @@ template <int V, bool FC1, int WM>
 __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds, const Tile tile,
                                               const int nt) {
   using namespace dma;
-  static_assert(fp8_x_fp4(V), "MXFP4 weights x E4M3 activations only");
+  static_assert(scaled_fp4(V), "MXFP4 weights x E4M3 or E2M1 activations only");
   constexpr bool MXA = a_blockscaled(V);
+  constexpr bool A4 = a_fp4(V);
+  constexpr int AF = a_fmt(V);
   constexpr int WN = kWN;
-  using L = Map<WM, MXA>;
+  using L = Map<WM, MXA, A4>;
+  constexpr int NF = L::kNF;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = lane_id();
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int row_end = tile.row0 + tile.nrows;
@@ -605,12 +620,17 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   for (int u = 0; u < kBPW; ++u) wcol[u] = wbase + min(nbb + kBPW * wave + u, nb_last) * KS * 1024;
 
   auto issue_a = [&](int ks, int stage) __attribute__((always_inline)) {
-    const uint32_t dst = lds0 + L::kAOff + stage * L::kABuf + wave * 2048;
-    lds_dma16(arow0 + ks * kKStep, dst);
-    lds_dma16(arow0 + ks * kKStep + kAHalf, dst + 1024);
-    if (two_rg) {
-      lds_dma16(arow1 + ks * kKStep, dst + kNW * 2048);
-      lds_dma16(arow1 + ks * kKStep + kAHalf, dst + kNW * 2048 + 1024);
+    const uint32_t dst = lds0 + L::kAOff + stage * L::kABuf + wave * (NF * 1024);
+    if constexpr (A4) {  // one fragment per 16 rows: k = 32 (L/16) + [0, 32)
+      lds_dma16(arow0 + ks * (kKStep / 2), dst);
+      if (two_rg) lds_dma16(arow1 + ks * (kKStep / 2), dst + kNW * 1024);
+    } else {
+      lds_dma16(arow0 + ks * kKStep, dst);
+      lds_dma16(arow0 + ks * kKStep + kAHalf, dst + 1024);
+      if (two_rg) {
+        lds_dma16(arow1 + ks * kKStep, dst + kNW * 2048);
+        lds_dma16(arow1 + ks * kKStep + kAHalf, dst + kNW * 2048 + 1024);
+      }
     }
   };
   auto issue_b = [&](int ks, int stage) __attribute__((always_inline)) {
@@ -670,18 +690,23 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
       const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
       bop[j] = fp4_operand(b);
     }
-    const uint8_t* as = lds + L::kAOff + (S & 1) * L::kABuf + (wm * WM) * 2048 + lane * 16;
+    const uint8_t* as = lds + L::kAOff + (S & 1) * L::kABuf + (wm * WM) * (NF * 1024) + lane * 16;
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       if (cols && i < nvalid) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(as + i * 2048);
-        const uint4 hi = *reinterpret_cast<const uint4*>(as + i * 2048 + 1024);
-        const v8i aop = as_v8i(lo, hi);
+        const uint4 lo = *reinterpret_cast<const uint4*>(as + i * (NF * 1024));
+        v8i aop;
+        if constexpr (A4) {
+          aop = fp4_operand(lo);
+        } else {
+          const uint4 hi = *reinterpret_cast<const uint4*>(as + i * 2048 + 1024);
+          aop = as_v8i(lo, hi);
+        }
         const int ax = MXA ? *reinterpret_cast<const int*>(sa + i * 256) : 127;
 #pragma unroll
         for (int j = 0; j < WN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              aop, bop[j], acc[i][j], 0, 4, MXA ? S : 0, ax, S, (int)sx[j]);
+              aop, bop[j], acc[i][j], AF, 4, MXA ? S : 0, ax, S, (int)sx[j]);
       }
     }
     // the loads of step ks+1 (A issued above, weights one step earlier) have
@@ -716,7 +741,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
 
 template <int V, bool FC1, int WM>
 __global__ __launch_bounds__(dma::kNW * kWave, 1) void k_gemm_dma(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[dma::Map<WM, a_blockscaled(V)>::kBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[dma::Map<WM, a_blockscaled(V), a_fp4(V)>::kBytes];
   Tile tile;
   int nt;
   if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
@@ -726,8 +751,8 @@ __global__ __launch_bounds__(dma::kNW * kWave, 1) void k_gemm_dma(GemmParams p) 
 template <int V, bool FC1>
 static hipError_t launch_v(int cfg, const GemmParams& p, int64_t blocks, hipStream_t st) {
   if (cfg == 1) k_gemm_lds<V, FC1, 4, 1, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p);
-  else if constexpr (fp8_x_fp4(V))  // 160 x 512; 128 x 512 with MXFP8 scales (registers)
-    k_gemm_dma<V, FC1, a_blockscaled(V) ? 4 : 5><<<(unsigned)blocks, dma::kNW * kWave, 0, st>>>(p);
+  else if constexpr (scaled_fp4(V))  // 160 x 512; 128 x 512 with MXFP8 scales (registers)
+    k_gemm_dma<V, FC1, V == kMxfp4Mxfp8 ? 4 : 5><<<(unsigned)blocks, dma::kNW * kWave, 0, st>>>(p);
   else k_gemm_ab<V, FC1, 8, 2, 4, 4><<<(unsigned)blocks, 512, 0, st>>>(p);
   return hipGetLastError();
 }
@@ -742,6 +767,8 @@ hipError_t launch_gemm_lds(int variant, bool fc1, int cfg, const GemmParams& p,
                                : launch_v<kMxfp4Fp8, false>(cfg, p, blocks, st);
     case kMxfp4Mxfp8: return fc1 ? launch_v<kMxfp4Mxfp8, true>(cfg, p, blocks, st)
                                  : launch_v<kMxfp4Mxfp8, false>(cfg, p, blocks, st);
+    case kMxfp4Mxfp4: return fc1 ? launch_v<kMxfp4Mxfp4, true>(cfg, p, blocks, st)
+                                 : launch_v<kMxfp4Mxfp4, false>(cfg, p, blocks, st);
     case kInt4Fp8: return fc1 ? launch_v<kInt4Fp8, true>(cfg, p, blocks, st)
                               : launch_v<kInt4Fp8, false>(cfg, p, blocks, st);
     default: return hipErrorInvalidValue;

@@ -35,11 +35,6 @@ __device__ __forceinline__ int64_t canon_row(int64_t dn, int32_t N, bool inter) 
   return (db & 1) * (N / 2) + (db >> 1) * 16 + r;
 }
 
-__device__ __forceinline__ uint32_t mx_code(float v_abs) {
-  // nearest E2M1 magnitude code, ties to even code
-  return (v_abs > 0.25f) + (v_abs >= 0.75f) + (v_abs > 1.25f) + (v_abs >= 1.75f) +
-         (v_abs > 2.5f) + (v_abs >= 3.5f) + (v_abs > 5.0f);
-}
 
 // thread per (device row, 32-block)
 __global__ __launch_bounds__(256) void k_prepare_mxfp4(const float* __restrict__ w, int32_t N,
@@ -78,7 +73,7 @@ __global__ __launch_bounds__(256) void k_prepare_mxfp4(const float* __restrict__
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const uint32_t sgn = (__float_as_uint(v[i]) >> 31) << 3;
-    const uint32_t c = mx_code(fabsf(v[i]) * inv) | sgn;
+    const uint32_t c = e2m1_magnitude_code(fabsf(v[i]) * inv) | sgn;
     out[i / 8] |= c << (4 * (i % 8));
   }
   const int KS = K / kKStep, KS4 = (KS + 3) / 4;

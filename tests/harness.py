@@ -88,10 +88,12 @@ class Problem:
         r["row_token"] = view(L.row_token, np.int32, rows)
         r["slot_row"] = view(L.slot_row, np.int32, rows).reshape(T, k)
         e4m3 = wl.afmt in ("fp8", "mxfp8")
-        if e4m3:
-            r["token_codes"] = view(L.tok_codes, np.uint8, T * wl.hidden).reshape(T, wl.hidden)
+        e2m1 = wl.afmt == "mxfp4"
+        if e4m3 or e2m1:
+            hc = wl.hidden // 2 if e2m1 else wl.hidden  # E2M1: two codes per byte
+            r["token_codes"] = view(L.tok_codes, np.uint8, T * hc).reshape(T, hc)
             r["token_scales"] = view(L.tok_scales, np.float32, T)
-        if wl.afmt == "mxfp8":
+        if wl.afmt in ("mxfp8", "mxfp4"):
             rb = mx_scale_row_bytes(wl.hidden)
             r["token_block_scales"] = mx_scales_canonical(
                 view(L.tok_bscales, np.uint8, T * rb).reshape(T, rb), wl.hidden)
@@ -99,12 +101,14 @@ class Problem:
             r["fc2_block_scales"] = mx_scales_canonical(
                 view(L.fc2_bscales, np.uint8, rows * rb).reshape(rows, rb), wl.inter)
         r["h"] = view(L.h, np.float32, rows * wl.inter).reshape(rows, wl.inter)
-        qdt = np.uint8 if e4m3 else np.uint16
-        r["fc2_codes"] = view(L.fc2_codes, qdt, rows * wl.inter).reshape(rows, wl.inter)
+        qdt = np.uint8 if e4m3 or e2m1 else np.uint16
+        ic = wl.inter // 2 if e2m1 else wl.inter
+        r["fc2_codes"] = view(L.fc2_codes, qdt, rows * ic).reshape(rows, ic)
         r["fc2_scales"] = view(L.fc2_scales, np.float32, rows)
         r["y2"] = view(L.y2, np.float32, rows * wl.hidden).reshape(rows, wl.hidden)
         r["num_tiles"] = int(view(L.num_tiles, np.int32, 1)[0])
         r["tile_m"] = L.tile_m
+        r["gemm_cfg"] = L.gemm_cfg
         tl = view(L.tiles, np.int32, 4 * L.max_tiles).reshape(-1, 4)
         r["tiles"] = tl[:r["num_tiles"], :3].copy()
         return r
@@ -171,8 +175,8 @@ def compare_all(g, r, wl, exact_rows=True):
     if wl.afmt == "fp8":
         assert np.array_equal(g["token_codes"], r["token_codes"]), "token E4M3 codes differ"
         assert np.array_equal(g["token_scales"].view(np.uint32), r["token_scales"].view(np.uint32))
-    if wl.afmt == "mxfp8":
-        assert np.array_equal(g["token_codes"], r["token_codes"]), "token E4M3 codes differ"
+    if wl.afmt in ("mxfp8", "mxfp4"):
+        assert np.array_equal(g["token_codes"], r["token_codes"]), "token element codes differ"
         assert np.array_equal(g["token_block_scales"], r["token_block_scales"]), "token E8M0 differ"
     assert rel_l2(g["h"], r["h"]) <= 1e-4, rel_l2(g["h"], r["h"])
     # FC2 input: h differs from the oracle's by float32 rounding, so a few
@@ -183,12 +187,13 @@ def compare_all(g, r, wl, exact_rows=True):
         dq = F.e4m3_decode(g["fc2_codes"]) * g["fc2_scales"][:, None]
         dr = F.e4m3_decode(r["fc2_codes"]) * r["fc2_scales"][:, None]
         assert rel_l2(dq, dr) <= 1e-3
-    if wl.afmt == "mxfp8":
+    if wl.afmt in ("mxfp8", "mxfp4"):
         same = np.mean(g["fc2_codes"] == r["fc2_codes"])
         assert same > 0.97, same
         assert np.mean(g["fc2_block_scales"] == r["fc2_block_scales"]) > 0.99
-        dq = Q.mxfp8_decode(g["fc2_codes"], g["fc2_block_scales"])
-        dr = Q.mxfp8_decode(r["fc2_codes"], r["fc2_block_scales"])
+        dec = Q.mxfp8_decode if wl.afmt == "mxfp8" else Q.mxfp4_decode
+        dq = dec(g["fc2_codes"], g["fc2_block_scales"])
+        dr = dec(r["fc2_codes"], r["fc2_block_scales"])
         assert rel_l2(dq, dr) <= 1e-3
     assert rel_l2(g["y2"], r["y2"]) <= 2e-3, rel_l2(g["y2"], r["y2"])
     return check_output(g["out"], r["out"])

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == set(M.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 def _d(**kw):
@@ -51,7 +51,7 @@ def test_weight_sizes(L):
 @pytest.mark.parametrize("kw,status", [
     (dict(hidden=100), 1), (dict(inter=0), 1), (dict(num_experts=0), 1),
     (dict(num_experts=2000), 1), (dict(wfmt="int4", afmt="bf16"), 2),
-    (dict(wfmt="int4", afmt="mxfp8"), 2)])
+    (dict(wfmt="int4", afmt="mxfp8"), 2), (dict(wfmt="int4", afmt="mxfp4"), 2)])
 def test_bad_dims(L, kw, status):
     with pytest.raises(M.MoeError) as ei:
         M.weights_query(_d(**kw))
@@ -112,6 +112,64 @@ def test_workspace_layout_mxfp8(L):
     lay = M.workspace_layout(_d(num_experts=8, hidden=384, inter=256, afmt="mxfp8"), 100, 2)
     assert lay.fc2_bscales - lay.tok_bscales >= 100 * 16
     assert M.workspace_layout(_d(), 4096, 8).tok_bscales == M.workspace_layout(_d(), 4096, 8).fc2_bscales
+
+
+def test_tune_table(L):
+    """Tuned tile configurations: per shape, top-k and token bucket
+    ceil(log2 T); the workspace size never changes."""
+    d = _d()
+    M.tune_clear()
+    base = M.workspace_layout(d, 4096, 8)
+    assert base.gemm_cfg == 2
+    try:
+        M.tune_set(d, 4096, 8, 1)
+        lay = M.workspace_layout(d, 4096, 8)
+        assert lay.gemm_cfg == 1 and lay.tile_m == 64 and lay.total == base.total
+        assert M.workspace_layout(d, 2049, 8).gemm_cfg == 1      # same bucket (2^12)
+        assert M.workspace_layout(d, 2048, 8).gemm_cfg == 2      # bucket 2^11: default
+        assert M.workspace_layout(d, 4096, 6).gemm_cfg == 2      # other top-k
+        assert M.workspace_layout(_d(afmt="bf16"), 4096, 8).gemm_cfg == 2  # other format
+        M.tune_set(d, 4096, 8, 0)
+        lay = M.workspace_layout(d, 4096, 8)
+        assert lay.tile_m == 16 and lay.total == base.total
+        assert lay.max_tiles == 4096 * 8 // 16 + 256
+        M.tune_set(d, 4096, 8, -1)                                # removal
+        assert M.workspace_layout(d, 4096, 8).gemm_cfg == 2
+        for bad in (3, -2):
+            with pytest.raises(M.MoeError) as ei:
+                M.tune_set(d, 4096, 8, bad)
+            assert ei.value.status == 1
+        with pytest.raises(M.MoeError):
+            M.tune_set(d, 0, 8, 1)
+        M.tune_set(d, 4096, 8, 1)
+        M.tune_clear()
+        assert M.workspace_layout(d, 4096, 8).gemm_cfg == 2
+    finally:
+        M.tune_clear()
+
+
+def test_autotune_rejects_bad_args(L):
+    d = _d(num_experts=8, hidden=256, inter=512).c()
+    ok = ctypes.c_void_p(0x1000)
+    chosen = ctypes.c_int32()
+    # iters out of range and null result pointer fail before touching the device
+    assert L.moe_autotune(ctypes.byref(d), ok, 4, ok, ok, ok, 2, 0, ctypes.byref(chosen), None,
+                          None) == 1
+    assert L.moe_autotune(ctypes.byref(d), ok, 4, ok, ok, ok, 2, 5, None, None, None) == 1
+    assert L.moe_autotune(ctypes.byref(d), ok, 0, ok, ok, ok, 2, 5, ctypes.byref(chosen), None,
+                          None) == 1
+
+
+def test_workspace_layout_w4a4(L):
+    # MXFP4 activations: packed E2M1 codes (half a byte each) plus the same
+    # block-scale regions as MXFP8
+    a = M.workspace_layout(_d(afmt="mxfp4"), 4096, 8)
+    b = M.workspace_layout(_d(afmt="mxfp8"), 4096, 8)
+    assert a.tok_scales - a.tok_codes >= 4096 * 7168 // 2
+    assert a.fc2_scales - a.fc2_codes >= 4096 * 8 * 2048 // 2
+    assert a.total < b.total
+    assert a.fc2_bscales - a.tok_bscales == b.fc2_bscales - b.tok_bscales
+    assert a.tile_m == 160 and a.gemm_cfg == 2
 
 
 def test_trace_modes(L):

@@ -17,7 +17,7 @@ from tests.harness import Problem, check_output, expected_work_map, rel_l2
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 CASES = ["dsv3_decode_mxfp4_bf16", "dsv3_int4_fp8", "dsv3_prefill_mxfp4_fp8",
-         "dsv4pro_prefill_mxfp4_fp8", "dsv3_prefill_mxfp4_mxfp8"]
+         "dsv4pro_prefill_mxfp4_fp8", "dsv3_prefill_mxfp4_mxfp8", "dsv3_prefill_mxfp4_mxfp4"]
 SAMPLE = 3  # tokens checked against the oracle end to end
 
 
@@ -77,8 +77,9 @@ def test_fullsize_sampled(name):
         q, s = O.quant.e4m3_rows(F.bf16_to_f32(p.hidden))
         assert np.array_equal(g["token_codes"], q)
         assert np.array_equal(g["token_scales"].view(np.uint32), s.view(np.uint32))
-    if wl.afmt == "mxfp8":
-        q, sx = O.quant.mxfp8_rows(F.bf16_to_f32(p.hidden))
+    if wl.afmt in ("mxfp8", "mxfp4"):
+        quant = O.quant.mxfp8_rows if wl.afmt == "mxfp8" else O.quant.mxfp4_quantize
+        q, sx = quant(F.bf16_to_f32(p.hidden))
         assert np.array_equal(g["token_codes"], q)
         assert np.array_equal(g["token_block_scales"], sx)
     # prepared weight codes of two experts

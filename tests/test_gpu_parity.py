@@ -31,6 +31,12 @@ SMALL = [
     (400, 4, 2, 384, 640, "mxfp4", "mxfp8", 33, 1.0), # full + ragged 128-row tiles, N tail
     (9, 40, 4, 512, 128, "mxfp4", "mxfp8", 34, 0.0),  # 16-row tiles, empty experts
     (6, 1, 1, 8320, 4224, "mxfp4", "mxfp8", 35, 0.0), # long rows, 17 scale groups (last partial)
+    # W4A4 (MXFP4 activations): every tile configuration, partial scale groups
+    (70, 6, 3, 384, 256, "mxfp4", "mxfp4", 51, 0.0),  # 64-row tiles
+    (300, 5, 2, 256, 384, "mxfp4", "mxfp4", 52, 2.0), # 160-row tiles, tails
+    (400, 4, 2, 384, 640, "mxfp4", "mxfp4", 53, 1.0), # full + ragged 160-row tiles, N tail
+    (9, 40, 4, 512, 128, "mxfp4", "mxfp4", 54, 0.0),  # 16-row tiles, empty experts
+    (6, 1, 1, 8320, 4224, "mxfp4", "mxfp4", 55, 0.0), # long rows
 ]
 
 
