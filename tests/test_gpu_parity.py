@@ -23,6 +23,7 @@ SMALL = [
     (9, 40, 4, 512, 128, "mxfp4", "bf16", 18, 0.0),
     (9, 40, 4, 512, 128, "int4", "fp8", 19, 0.0),
     (1, 3, 3, 128, 128, "mxfp4", "fp8", 20, 0.0),     # single token, k = E
+    (40, 1024, 16, 128, 128, "mxfp4", "fp8", 24, 0.0),  # the most experts and the largest top-k
     (6, 1, 1, 8320, 4224, "mxfp4", "fp8", 23, 0.0),   # rows longer than the quantisers keep in registers
     # MXFP8 activations: every tile configuration, K not a multiple of 512
     # (a partial 4-step scale group), ragged row and N tails
