@@ -1,6 +1,6 @@
 // Register-direct grouped GEMM of the fused MoE (gfx950): each wave loads its
 // own activation and weight fragments straight into MFMA operand registers,
-// one K step ahead.  Used for BF16 activations (the weights are expanded from
+// one or two K steps ahead.  Used for BF16 activations (the weights are expanded from
 // E2M1 to bf16 in registers with the E8M0 scale folded in) and for the 16-row
 // tiles of decode-sized batches, where the weight stream from HBM dominates.
 #include "moe_gemm_common.h"
@@ -19,11 +19,14 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   Tile tile;
   int nt;
   if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
-  const int wave = threadIdx.x / kWave, lane = lane_id();
+  // wave-uniform values are made scalar: a branch on a per-lane value is an
+  // exec-masked branch, after which the compiler waits for every outstanding
+  // load (that drained the one-step prefetch before each step's MFMAs)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = lane_id();
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int row_base = tile.row0 + 16 * WM * wm;
   const int row_end = tile.row0 + tile.nrows;
-  const int nvalid = min(WM, (row_end - row_base + 15) / 16);
+  const int nvalid = __builtin_amdgcn_readfirstlane(min(WM, (row_end - row_base + 15) / 16));
   if (nvalid <= 0) return;
 
   const int K = p.K;
@@ -32,8 +35,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   const uint8_t* wbase = p.w + e * p.w_expert_stride;
   const uint8_t* sbase = p.s + e * p.s_expert_stride;
   const int64_t nb0 = (int64_t)nt * (WAVES_N * WN) + wn * WN;
-  const int jvalid = (int)min<int64_t>(WN, p.N / 16 - nb0);  // N tail: 16-column blocks left
+  // N tail: 16-column blocks left
+  const int jvalid = __builtin_amdgcn_readfirstlane((int)min<int64_t>(WN, p.N / 16 - nb0));
   if (jvalid <= 0) return;
+  const int64_t nb_last = p.N / 16 - 1;
 
   // A row pointers (rows past the tile end re-read its last row; their
   // outputs are never stored)
@@ -64,33 +69,33 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   uint32_t scc[WN], scn[WN];  // E8M0 dword (MXFP4) or float bits (INT4 group scale)
   uint32_t asc[WM], asn[WM];  // E8M0 A scale of this lane's row and k-block (MXFP8)
 
+  // Loads are unconditional (subtiles past the tile end re-read its last row,
+  // column blocks past N the last block; neither is stored), so no branch
+  // sits between a load and its use.
   auto load = [&](int ks, uint4 (&a)[WM][NA], uint4 (&b)[WN], uint32_t (&sc)[WN],
                   uint32_t (&as)[WM]) {
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
-      if (i < nvalid) {
-        if (a_fp4(V)) {
-          a[i][0] = *reinterpret_cast<const uint4*>(arow[i] + ks * (kKStep / 2));
+      if (a_fp4(V)) {
+        a[i][0] = *reinterpret_cast<const uint4*>(arow[i] + ks * (kKStep / 2));
+        as[i] = *reinterpret_cast<const uint32_t*>(asrow[i] + 16 * (ks >> 2));
+      } else if (scaled_fp4(V)) {
+        a[i][0] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep);
+        a[i][1] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep + 64);
+        if (a_blockscaled(V))
           as[i] = *reinterpret_cast<const uint32_t*>(asrow[i] + 16 * (ks >> 2));
-        } else if (scaled_fp4(V)) {
-          a[i][0] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep);
-          a[i][1] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep + 64);
-          if (a_blockscaled(V))
-            as[i] = *reinterpret_cast<const uint32_t*>(asrow[i] + 16 * (ks >> 2));
-        } else if (V == kInt4Fp8) {
-          a[i][0] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep);
-          a[i][1] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep + 16);
-        } else {
+      } else if (V == kInt4Fp8) {
+        a[i][0] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep);
+        a[i][1] = *reinterpret_cast<const uint4*>(arow[i] + ks * kKStep + 16);
+      } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            a[i][q] = *reinterpret_cast<const uint4*>(arow[i] + 2 * ks * kKStep + 16 * q);
-        }
+        for (int q = 0; q < 4; ++q)
+          a[i][q] = *reinterpret_cast<const uint4*>(arow[i] + 2 * ks * kKStep + 16 * q);
       }
     }
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      if (j >= jvalid) continue;
-      const int64_t nb = nb0 + j;
+      const int64_t nb = min(nb0 + j, nb_last);
       b[j] = *reinterpret_cast<const uint4*>(wbase + ((nb * KS + ks) * 64 + lane) * 16);
       if (V == kInt4Fp8)
         sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS + ks) * 16 + (lane & 15)) * 4);
@@ -161,14 +166,37 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     }
   };
 
-  load(0, ac, bc, scc, asc);
-  for (int ks = 0; ks < KS; ks += 2) {
-    if (ks + 1 < KS) load(ks + 1, an, bn, scn, asn);
-    compute(ks, ac, bc, scc, asc);
-    if (ks + 1 < KS) {
-      if (ks + 2 < KS) load(ks + 2, ac, bc, scc, asc);
+  // Prefetch step indices are clamped (the last step is reloaded, unused) so
+  // every iteration issues the same loads and no load sits under a branch.
+  // 16-row tiles (one subtile per wave, few registers) load two steps ahead
+  // through three register sets (2 % faster on the decode GEMMs than one
+  // step ahead); larger tiles one step ahead through two.
+  int ks = 0;
+  if constexpr (WM == 1) {
+    uint4 a2[WM][NA];
+    uint4 b2[WN];
+    uint32_t sc2[WN], as2[WM];
+    load(0, ac, bc, scc, asc);
+    load(min(1, KS - 1), an, bn, scn, asn);
+    for (; ks + 3 <= KS; ks += 3) {
+      load(min(ks + 2, KS - 1), a2, b2, sc2, as2);
+      compute(ks, ac, bc, scc, asc);
+      load(min(ks + 3, KS - 1), ac, bc, scc, asc);
+      compute(ks + 1, an, bn, scn, asn);
+      load(min(ks + 4, KS - 1), an, bn, scn, asn);
+      compute(ks + 2, a2, b2, sc2, as2);
+    }
+    if (ks < KS) compute(ks, ac, bc, scc, asc);
+    if (ks + 1 < KS) compute(ks + 1, an, bn, scn, asn);
+  } else {
+    load(0, ac, bc, scc, asc);
+    for (; ks + 2 <= KS; ks += 2) {
+      load(min(ks + 1, KS - 1), an, bn, scn, asn);
+      compute(ks, ac, bc, scc, asc);
+      load(min(ks + 2, KS - 1), ac, bc, scc, asc);
       compute(ks + 1, an, bn, scn, asn);
     }
+    if (ks < KS) compute(ks, ac, bc, scc, asc);
   }
 
   epilogue<FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
