@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -104,7 +104,9 @@ typedef struct {
  *   y2          float  [T*k, H] GEMM2 output per expanded row
  *   num_tiles   int32  [1]      GEMM work-map length; tile_m rows per tile
  * gemm_cfg is the tile configuration the call uses (tuned or default, see
- * moe_tune_set), max_tiles the bound on its work-map length. */
+ * moe_tune_set), max_tiles the bound on its work-map length.  fc2_fused = 1:
+ * GEMM1 quantises its output to the FC2 input itself (MX activation formats
+ * with gemm_cfg 1-2), so h is not written and fc2_scales are not set. */
 typedef struct {
   size_t total;
   size_t ids, topk_w, chunk_counts, offsets, row_token, slot_row, tiles, num_tiles;
@@ -113,6 +115,7 @@ typedef struct {
   int32_t gemm_cfg;
   int64_t max_tiles;
   size_t tok_bscales, fc2_bscales;
+  int32_t fc2_fused;
 } moe_ws_layout;
 
 int32_t moe_abi_version(void);
@@ -236,7 +239,7 @@ typedef enum {
   MOE_STAGE_ROUTE = 0,    /* router, routing index, work map */
   MOE_STAGE_QUANT = 1,    /* per-token E4M3 quantisation (FP8 activations) */
   MOE_STAGE_GEMM1 = 2,    /* grouped GEMM1 + SwiGLU */
-  MOE_STAGE_REQUANT = 3,  /* FC2 input */
+  MOE_STAGE_REQUANT = 3,  /* FC2 input (nothing when GEMM1 writes it, fc2_fused) */
   MOE_STAGE_GEMM2 = 4,    /* grouped GEMM2 */
   MOE_STAGE_FINALIZE = 5, /* router-weighted top-k sum */
   MOE_NUM_STAGES = 6

@@ -45,7 +45,8 @@ class WsLayout(ctypes.Structure):
         "total", "ids", "topk_w", "chunk_counts", "offsets", "row_token", "slot_row", "tiles",
         "num_tiles", "tok_codes", "tok_scales", "h", "fc2_codes", "fc2_scales", "y2")] + [
         ("tile_m", ctypes.c_int32), ("gemm_cfg", ctypes.c_int32), ("max_tiles", ctypes.c_int64),
-        ("tok_bscales", ctypes.c_size_t), ("fc2_bscales", ctypes.c_size_t)]
+        ("tok_bscales", ctypes.c_size_t), ("fc2_bscales", ctypes.c_size_t),
+        ("fc2_fused", ctypes.c_int32)]
 
 
 _lib = None

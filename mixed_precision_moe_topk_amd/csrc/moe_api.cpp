@@ -212,6 +212,7 @@ moe_status layout_of(const moe_dims* d, int64_t T, int32_t k, moe_ws_layout* L, 
   L->tile_m = tile_m;
   L->gemm_cfg = cfg;
   L->max_tiles = max_tiles;
+  L->fc2_fused = mx && cfg != 0;  // waves of tiles 1-2 hold whole 32-column blocks of h
   return MOE_OK;
 }
 
@@ -497,16 +498,23 @@ moe_status run_checked(const moe_dims* dims, const void* hidden, int64_t num_tok
   g1.n_tiles = (int32_t)cdiv(2 * I, cfg.bn());
   g1.out = h;
   g1.out_stride = I;
+  uint8_t* q2 = ws + L.fc2_codes;
+  float* s2 = reinterpret_cast<float*>(ws + L.fc2_scales);
+  uint8_t* b2 = mx ? ws + L.fc2_bscales : nullptr;
+  // MX formats with tiles of 1-2: GEMM1 writes the FC2 input itself
+  g1.q_out = L.fc2_fused ? q2 : nullptr;
+  g1.q_stride = e2m1 ? I / 2 : I;
+  g1.q_bscales = L.fc2_fused ? b2 : nullptr;
+  g1.q_bstride = moe::mx_scale_row_bytes(I);
   MOE_TRY(hip_check(moe::launch_gemm(variant, true, L.gemm_cfg, g1, L.max_tiles, stream),
                     "gemm1", stream));
   trace_mark(tc, 3, stream);
 
-  uint8_t* q2 = ws + L.fc2_codes;
-  float* s2 = reinterpret_cast<float*>(ws + L.fc2_scales);
-  uint8_t* b2 = mx ? ws + L.fc2_bscales : nullptr;
-  const int rq_mode = fp8 ? moe::kQuantFp8Row : (mx ? mx_mode : moe::kQuantBf16);
-  MOE_TRY(hip_check(moe::launch_requant(h, rows, I, rq_mode, q2, s2, b2, stream),
-                    "fc2 requant", stream));
+  if (!L.fc2_fused) {
+    const int rq_mode = fp8 ? moe::kQuantFp8Row : (mx ? mx_mode : moe::kQuantBf16);
+    MOE_TRY(hip_check(moe::launch_requant(h, rows, I, rq_mode, q2, s2, b2, stream),
+                      "fc2 requant", stream));
+  }
   trace_mark(tc, 4, stream);
 
   float* y2 = reinterpret_cast<float*>(ws + L.y2);
@@ -517,6 +525,10 @@ moe_status run_checked(const moe_dims* dims, const void* hidden, int64_t num_tok
   g2.row_scale = fp8 ? s2 : nullptr;
   g2.a_scale = b2;
   g2.a_scale_stride = moe::mx_scale_row_bytes(I);
+  g2.q_out = nullptr;
+  g2.q_stride = 0;
+  g2.q_bscales = nullptr;
+  g2.q_bstride = 0;
   g2.w = wbytes + s.w1_codes;
   g2.w_expert_stride = s.codes_per_expert;
   g2.s = sbytes + s.w1_scales;

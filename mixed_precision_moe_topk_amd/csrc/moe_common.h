@@ -78,6 +78,18 @@ __device__ __forceinline__ uint32_t e2m1_magnitude_code(float v_abs) {
          (v_abs > 2.5f) + (v_abs >= 3.5f) + (v_abs > 5.0f);
 }
 
+// OCP MX shared exponent of a 32-element block: floor(log2 amax) - EMAX
+// (EMAX 8 for E4M3 elements, 2 for E2M1), clamped to [-127, 127]; 0 for an
+// all-zero block (E8M0 code 127).
+template <int EMAX>
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const uint32_t b = __float_as_uint(amax);
+  const int e = (int)((b >> 23) & 0xFFu);
+  const int fl = e ? e - 127 : (31 - __clz(b & 0x7FFFFFu)) - 149;  // floor(log2 amax)
+  return min(max(fl - EMAX, -127), 127);
+}
+
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
   const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
   const float a = fminf(fabsf(v), 448.0f);
@@ -162,6 +174,13 @@ struct GemmParams {
   int32_t N;                   // device columns (FC1: 2I interleaved gate/up; FC2: H)
   float* out;                  // FC1: h [rows, N/2]; FC2: y2 [rows, N]
   int64_t out_stride;          // floats per output row
+  // FC1 with MX activations and tiles whose waves hold whole 32-column
+  // blocks of h: when q_out is set, the epilogue writes the FC2 input (E4M3 or
+  // packed E2M1 codes + E8M0 codes in MFMA scale order) instead of h
+  uint8_t* q_out;
+  int64_t q_stride;            // bytes per q_out row
+  uint8_t* q_bscales;
+  int64_t q_bstride;           // bytes per q_bscales row (mx_scale_row_bytes(N/2))
 };
 
 // E8M0 block scales of MXFP8 activations, stored in the order the block-scaled

@@ -152,14 +152,6 @@ __global__ __launch_bounds__(256) void k_requant(const float* __restrict__ h, in
 // flashinfer PR #4793, "Unify MoE CuTe DSL dispatch to be dtype agnostic",
 // and PR #3614's MXFP8xMXFP8; the MXFP4 activation pack of PR #4793's w4a4
 // mode, quantised like the weights.)
-template <int EMAX>
-__device__ __forceinline__ int mx_exponent(float amax) {
-  if (!(amax > 0.0f)) return 0;
-  const uint32_t b = __float_as_uint(amax);
-  const int e = (int)((b >> 23) & 0xFFu);
-  const int fl = e ? e - 127 : (31 - __clz(b & 0x7FFFFFu)) - 149;  // floor(log2 amax)
-  return min(max(fl - EMAX, -127), 127);
-}
 
 // Eight consecutive elements per thread, four threads (consecutive lanes) per
 // 32-element block.  `valid`: the group's block lies inside the row (rows are

@@ -187,6 +187,76 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const v4f (&acc)[W
   }
 }
 
+// FC1 epilogue for MX activation formats that quantises the FC2 input in
+// place of writing h.  Intermediate blocks (2m, 2m+1) of a wave are the 32
+// columns of MX block nb0/4 + m (the wave's first device column block nb0 is a
+// multiple of 4 when WN % 4 == 0); lane l holds column l%16 of both halves for
+// rows 4(l/16) + v, so the block amax is a reduction over the 16 lanes of a
+// row group.  The h values, the exponent rule and the encoders are the ones
+// the separate FC2 quantiser uses, so the codes are the same bits.  Row
+// scales are 1 for these formats (the caller passes none).
+template <bool E2M1, int WM, int WN>
+__device__ __forceinline__ void epilogue_fc1_mx(const GemmParams& p, const v4f (&acc)[WM][WN],
+                                                int row_base, int row_end, int nvalid,
+                                                int64_t nb0, int jvalid, int lane) {
+  static_assert(WN % 4 == 0, "whole 32-column MX blocks per wave");
+  if (jvalid < WN) return;  // columns past N (N is a multiple of 256)
+  const int col_lane = lane & 15;
+  const int row_lane = 4 * (lane >> 4);
+#pragma unroll
+  for (int m = 0; m < WN / 4; ++m) {
+    const int64_t b = (nb0 >> 2) + m;  // MX block: h columns [32b, 32b + 32)
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      if (i >= nvalid) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = row_base + 16 * i + row_lane + v;
+        const float x0 = silu(acc[i][4 * m][v]) * acc[i][4 * m + 1][v];
+        const float x1 = silu(acc[i][4 * m + 2][v]) * acc[i][4 * m + 3][v];
+        float amax = fmaxf(fabsf(x0), fabsf(x1));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        amax = fmaxf(amax, __shfl_xor(amax, 4));
+        amax = fmaxf(amax, __shfl_xor(amax, 8));
+        const int x = mx_exponent<E2M1 ? 2 : 8>(amax);
+        const float inv = __uint_as_float((uint32_t)(127 - x) << 23);  // 2^-X
+        uint8_t* qrow = p.q_out + (int64_t)r * p.q_stride;
+        if (E2M1) {
+          const uint32_t n0 = e2m1_magnitude_code(fabsf(x0) * inv) | ((__float_as_uint(x0) >> 31) << 3);
+          const uint32_t n1 = e2m1_magnitude_code(fabsf(x1) * inv) | ((__float_as_uint(x1) >> 31) << 3);
+          const uint32_t o0 = __shfl_xor(n0, 1), o1 = __shfl_xor(n1, 1);  // odd column's nibble
+          if (r < row_end && !(col_lane & 1)) {
+            qrow[16 * b + col_lane / 2] = (uint8_t)(n0 | (o0 << 4));
+            qrow[16 * b + 8 + col_lane / 2] = (uint8_t)(n1 | (o1 << 4));
+          }
+        } else if (r < row_end) {
+          qrow[32 * b + col_lane] = (uint8_t)e4m3_encode(x0 * inv);
+          qrow[32 * b + 16 + col_lane] = (uint8_t)e4m3_encode(x1 * inv);
+        }
+        if (r < row_end && col_lane == 0)
+          p.q_bscales[(int64_t)r * p.q_bstride + mx_scale_offset(b)] = (uint8_t)(x + 127);
+      }
+    }
+  }
+}
+
+// End of a GEMM block: the fused FC1 + FC2-quantisation epilogue when the
+// caller asks for it (q_out set) and the format and tile allow it, else the
+// plain epilogue.
+template <int V, bool FC1, int WM, int WN>
+__device__ __forceinline__ void finish_tile(const GemmParams& p, const v4f (&acc)[WM][WN],
+                                            int row_base, int row_end, int nvalid, int64_t nb0,
+                                            int jvalid, int lane) {
+  if constexpr (FC1 && a_blockscaled(V) && WN % 4 == 0) {
+    if (p.q_out) {
+      epilogue_fc1_mx<a_fp4(V), WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+      return;
+    }
+  }
+  epilogue<FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+}
+
 hipError_t launch_gemm_direct(int variant, bool fc1, int cfg, const GemmParams& p,
                               int64_t max_tiles, hipStream_t st);
 hipError_t launch_gemm_lds(int variant, bool fc1, int cfg, const GemmParams& p,

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     if (ks < KS) compute(ks, ac, bc, scc, asc);
   }
 
-  epilogue<FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  finish_tile<V, FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
 

@@ -268,7 +268,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
   if (ks < KS) step(std::integral_constant<int, 0>{}, ks);
   if (ks + 1 < KS) step(std::integral_constant<int, 1>{}, ks + 1);
   if (ks + 2 < KS) step(std::integral_constant<int, 2>{}, ks + 2);
-  epilogue<FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  finish_tile<V, FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
 template <int V, bool FC1, int NW, int WAVES_M, int WM, int WN, int MINB = 2, int PB = 2,
@@ -485,7 +485,7 @@ __device__ __forceinline__ void gemm_ab_body(const GemmParams& p, uint8_t* lds, 
   if (ks < KS) step(std::integral_constant<int, 0>{}, ks);
   if (ks + 1 < KS) step(std::integral_constant<int, 1>{}, ks + 1);
   if (ks + 2 < KS) step(std::integral_constant<int, 2>{}, ks + 2);
-  epilogue<FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  finish_tile<V, FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
 template <int V, bool FC1, int NW, int WAVES_M, int WM, int WN, int MINB = 1>
@@ -736,7 +736,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   if (ks + 1 < KS) { step(std::integral_constant<int, 1>{}, ks + 1, bstage); bstage = bstage == 2 ? 0 : bstage + 1; }
   if (ks + 2 < KS) step(std::integral_constant<int, 2>{}, ks + 2, bstage);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  epilogue<FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  finish_tile<V, FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
 template <int V, bool FC1, int WM>

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == set(M.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
 
 
 def _d(**kw):

@@ -1,8 +1,9 @@
 """Tile-configuration selection on the GPU: every configuration of every format
 combination matches the oracle (forced through the tuning table, on skewed
 routing), the configurations give identical bits (each K step is accumulated
-in the same order by the same matrix instruction whatever the tile shape), and
-the autotuner validates, times and stores its choice."""
+in the same order by the same matrix instruction whatever the tile shape; the
+FC2 input that GEMM1 quantises itself for the MX formats equals the separate
+quantiser's), and the autotuner validates, times and stores its choice."""
 import numpy as np
 import pytest
 
@@ -36,8 +37,15 @@ def test_every_tile_config_matches_oracle(wf, af):
             runs[c] = g
     finally:
         M.tune_clear()
+    keys = ["fc2_codes", "y2", "out"]
+    if af in ("mxfp8", "mxfp4"):
+        # configurations 1-2 quantise the FC2 input inside GEMM1 (no h)
+        assert [runs[c]["fc2_fused"] for c in range(M.NUM_GEMM_CFG)] == [False, True, True]
+        keys.append("fc2_block_scales")
+    else:
+        keys.append("h")
     for c in range(1, M.NUM_GEMM_CFG):
-        for key in ("h", "y2", "out"):
+        for key in keys:
             assert np.array_equal(runs[c][key].view(np.uint8), runs[0][key].view(np.uint8)), (c, key)
 
 
