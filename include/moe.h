@@ -105,8 +105,8 @@ typedef struct {
  *   num_tiles   int32  [1]      GEMM work-map length; tile_m rows per tile
  * gemm_cfg is the tile configuration the call uses (tuned or default, see
  * moe_tune_set), max_tiles the bound on its work-map length.  fc2_fused = 1:
- * GEMM1 quantises its output to the FC2 input itself (MX activation formats
- * with gemm_cfg 1-2), so h is not written and fc2_scales are not set. */
+ * GEMM1 quantises its output to the FC2 input itself (MX activation formats),
+ * so h is not written and fc2_scales are not set. */
 typedef struct {
   size_t total;
   size_t ids, topk_w, chunk_counts, offsets, row_token, slot_row, tiles, num_tiles;

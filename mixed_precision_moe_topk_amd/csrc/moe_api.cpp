@@ -212,7 +212,8 @@ moe_status layout_of(const moe_dims* d, int64_t T, int32_t k, moe_ws_layout* L, 
   L->tile_m = tile_m;
   L->gemm_cfg = cfg;
   L->max_tiles = max_tiles;
-  L->fc2_fused = mx && cfg != 0;  // waves of tiles 1-2 hold whole 32-column blocks of h
+  // waves whose tiles hold whole 32-column blocks of h (4 column blocks)
+  L->fc2_fused = mx && moe::gemm_cfg(cfg, variant_of(d)).wn % 4 == 0;
   return MOE_OK;
 }
 
@@ -501,7 +502,7 @@ moe_status run_checked(const moe_dims* dims, const void* hidden, int64_t num_tok
   uint8_t* q2 = ws + L.fc2_codes;
   float* s2 = reinterpret_cast<float*>(ws + L.fc2_scales);
   uint8_t* b2 = mx ? ws + L.fc2_bscales : nullptr;
-  // MX formats with tiles of 1-2: GEMM1 writes the FC2 input itself
+  // MX formats: GEMM1 writes the FC2 input itself
   g1.q_out = L.fc2_fused ? q2 : nullptr;
   g1.q_stride = e2m1 ? I / 2 : I;
   g1.q_bscales = L.fc2_fused ? b2 : nullptr;

@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
 template <int V, bool FC1>
 static hipError_t launch_v(int cfg, const GemmParams& p, int64_t blocks, hipStream_t st) {
   switch (cfg) {
-    case 0: k_gemm<V, FC1, 1, 1, 2><<<(unsigned)blocks, 256, 0, st>>>(p); break;
+    case 0: k_gemm<V, FC1, 1, 1, 4><<<(unsigned)blocks, 256, 0, st>>>(p); break;
     case 1: k_gemm<V, FC1, 1, 3, 2><<<(unsigned)blocks, 256, 0, st>>>(p); break;
     default: k_gemm<V, FC1, 2, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p); break;
   }

@@ -170,6 +170,11 @@ def test_workspace_layout_w4a4(L):
     assert a.total < b.total
     assert a.fc2_bscales - a.tok_bscales == b.fc2_bscales - b.tok_bscales
     assert a.tile_m == 160 and a.gemm_cfg == 2
+    # GEMM1 quantises the FC2 input itself for the MX formats only
+    assert a.fc2_fused == 1 and b.fc2_fused == 1
+    assert M.workspace_layout(_d(afmt="mxfp4"), 64, 8).fc2_fused == 1
+    assert M.workspace_layout(_d(), 4096, 8).fc2_fused == 0
+    assert M.workspace_layout(_d(afmt="bf16"), 64, 8).fc2_fused == 0
 
 
 def test_trace_modes(L):

@@ -117,6 +117,33 @@ def test_router_ties_bit_exact(E, k, T):
     assert np.array_equal(g["slot_row"], slot_row.astype(np.int32))
 
 
+@pytest.mark.parametrize("af,lo,hi", [("fp8", -20, 20), ("bf16", -20, 20), ("mxfp8", -4, 4),
+                                      ("mxfp4", -6, 6)])
+def test_zero_and_extreme_token_rows(af, lo, hi):
+    """Token rows that are all zero (amax = 0: token scale 1 / E8M0 code 127),
+    a zero 32-element block inside a row, and rows scaled by 2^lo and 2^hi
+    (exact in bf16), through every stage; each group of rows is checked
+    against its own magnitude."""
+    from oracle import formats as F
+
+    wl = MI.small_workload(48, 6, 2, 256, 256, "mxfp4", af, 61, 0.0)
+    x = F.bf16_to_f32(MI.hidden_bf16(wl.seed, wl.tokens, wl.hidden)).copy()
+    x[0] = 0.0
+    x[1] = -0.0
+    x[2, :32] = 0.0
+    x[3:10] *= np.float32(2.0 ** lo)
+    x[10:17] *= np.float32(2.0 ** hi)
+    hb = F.bf16_rne(x)
+    assert np.array_equal(F.bf16_to_f32(hb), x)
+    p = Problem(wl, hidden=hb)
+    g = p.run_gpu()
+    r = p.run_oracle()
+    compare_all(g, r, wl)
+    assert np.all(F.bf16_to_f32(g["out"][:2]) == 0.0)
+    for rows in (slice(2, 3), slice(3, 10), slice(10, 17), slice(17, 48)):
+        check_output(g["out"][rows], r["out"][rows])
+
+
 def test_empty_batch_is_noop():
     import torch
 
