@@ -170,8 +170,10 @@ moe_status moe_workspace_layout(const moe_dims* dims, int64_t num_tokens, int32_
  *   weights, scales: prepared by moe_prepare_weights for all experts
  *   out:           device bf16 bits [num_tokens, hidden], fully overwritten
  *   workspace:     device buffer of at least moe_workspace_query bytes
- * num_tokens = 0 returns MOE_OK without launching.  No allocation and no
- * host synchronisation (unless MOE_SYNC_CHECK=1). */
+ * num_tokens = 0 returns MOE_OK without launching.  No allocation, no host
+ * synchronisation (unless MOE_SYNC_CHECK=1) and no memset: the call can be
+ * captured into a HIP graph (with stage timing off); the workspace needs no
+ * initialisation. */
 moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_tokens,
                       const float* router_logits, const void* weights, const void* scales,
                       int32_t top_k, void* out, void* workspace, size_t workspace_bytes,
