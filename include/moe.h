@@ -10,13 +10,17 @@
  *      logits ordered by the smaller expert index), weights = softmax over the
  *      k selected logits;
  *   2. FP8 activations: per-token E4M3 quantisation, s = amax/448, codes of
- *      x/s rounded to nearest even and saturated at 448; BF16 activations are
- *      used as they are;
+ *      x/s rounded to nearest even and saturated at 448; MXFP8 / MXFP4
+ *      activations: per 32 elements the OCP MX exponent X = floor(log2 amax)
+ *      - 8 / - 2 and E4M3 / E2M1 codes of x * 2^-X (flashinfer PR #4793,
+ *      Walkthrough: MXFP8 dispatch packing, MXFP4 activation pack); BF16
+ *      activations are used as they are;
  *   3. grouped GEMM1 (gate+up) over the routed rows of each expert, times the
  *      token scale, then h = silu(gate) * up in float32;
- *   4. FC2 input: FP8 activations -> per-row E4M3 of h (same quantiser);
- *      BF16 activations -> bf16(h);
- *   5. grouped GEMM2, times the row scale (float32 y2);
+ *   4. FC2 input: the activation format's quantiser applied to each row of h
+ *      (per-row E4M3, MXFP8 or MXFP4); BF16 activations -> bf16(h);
+ *   5. grouped GEMM2, times the row scale (float32 y2; block scales of the MX
+ *      formats are applied inside the matrix product);
  *   6. out[t] = bf16(sum over the k slots of weight * y2), float32 sum.
  *
  * Weight formats: MXFP4 (E2M1 codes, one E8M0 scale per 32 elements along K)
