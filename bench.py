@@ -129,7 +129,8 @@ def cpu_baseline(wl):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the layer runs on one GPU only (expert-parallel sharding "
+                                   "across GPUs is not implemented); --gpus must be 1"}))
         return 2
     import torch
 
