@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void k_requant(const float* __restrict__ h, in
   if (bf16_out) {
     uint2* out = reinterpret_cast<uint2*>(codes + r * I * 2);
     for (int i = threadIdx.x; i < nv; i += blockDim.x) {
-      const float4 v = row[i];
+      const float4 v = load_stream(row + i);
       out[i] = make_uint2(bf16_bits(v.x) | (bf16_bits(v.y) << 16),
                           bf16_bits(v.z) | (bf16_bits(v.w) << 16));
     }
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void k_requant(const float* __restrict__ h, in
 #pragma unroll
     for (int q = 0; q < kR; ++q) {
       const int i = threadIdx.x + 256 * q;
-      v[q] = i < nv ? row[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[q] = i < nv ? load_stream(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int q = 0; q < kR; ++q) amax = f4_amax(v[q], amax);
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ y2,
       float4 y[KC];
 #pragma unroll
       for (int j = 0; j < KC; ++j)
-        y[j] = reinterpret_cast<const float4*>(y2 + (int64_t)slot_row[t * KC + j] * H)[i];
+        y[j] = load_stream(reinterpret_cast<const float4*>(y2 + (int64_t)slot_row[t * KC + j] * H) + i);
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
         const float w = weights[t * KC + j];
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ y2,
     } else {
       for (int j = 0; j < k; ++j) {
         const float w = weights[t * k + j];
-        const float4 y = reinterpret_cast<const float4*>(y2 + (int64_t)slot_row[t * k + j] * H)[i];
+        const float4 y = load_stream(reinterpret_cast<const float4*>(y2 + (int64_t)slot_row[t * k + j] * H) + i);
         acc.x = __fadd_rn(acc.x, __fmul_rn(w, y.x));
         acc.y = __fadd_rn(acc.y, __fmul_rn(w, y.y));
         acc.z = __fadd_rn(acc.z, __fmul_rn(w, y.z));
