@@ -759,7 +759,7 @@ static hipError_t launch_v(int cfg, const GemmParams& p, int64_t blocks, hipStre
 
 hipError_t launch_gemm_lds(int variant, bool fc1, int cfg, const GemmParams& p,
                            int64_t max_tiles, hipStream_t st) {
-  const int64_t blocks = max_tiles * p.n_tiles;
+  const int64_t blocks = gemm_blocks(max_tiles, p.n_tiles);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   switch (variant) {
