@@ -96,10 +96,12 @@ typedef struct {
  *   tok_codes   uint8  [T, H]   E4M3 token codes (FP8 and MXFP8 activations);
  *                      [T, H/2] E2M1 codes, element 2i in the low nibble (MXFP4)
  *   tok_scales  float  [T]      token scales (FP8 activations; 1.0 for MX formats)
- *   h           float  [T*k, I] SwiGLU output per expanded row
+ *   h           float  [T*k, I] SwiGLU output per expanded row (not written
+ *                               when fc2_fused)
  *   fc2_codes   uint8  [T*k, I] E4M3 (FP8, MXFP8), [T*k, I/2] E2M1 (MXFP4) or
  *                               bf16 bits ([T*k, I] uint16)
- *   fc2_scales  float  [T*k]    per-row FC2 input scale (1.0 for BF16 and MX formats)
+ *   fc2_scales  float  [T*k]    per-row FC2 input scale (FP8; 1.0 for BF16; not
+ *                               written for the MX formats)
  *   tok_bscales uint8  [T, 16*ceil(H/512)]   E8M0 block scales of the token
  *                                  codes (MXFP8, MXFP4), in matrix-core order:
  *                                  the scale of elements [32b, 32b + 32) of a
