@@ -144,6 +144,29 @@ def test_zero_and_extreme_token_rows(af, lo, hi):
         check_output(g["out"][rows], r["out"][rows])
 
 
+@pytest.mark.parametrize("wf,af", [("mxfp4", "bf16"), ("int4", "fp8"), ("mxfp4", "mxfp8"),
+                                   ("mxfp4", "mxfp4")])
+def test_library_workspace_matches_caller_workspace(wf, af):
+    """moe_run (workspace kept by the library per device and stream, grown on
+    demand) gives the same bits as moe_run_ws, also after a smaller and a
+    larger call on the same stream."""
+    import torch
+
+    import mixed_precision_moe_topk_amd as M
+
+    outs = []
+    for T in (40, 8, 130):
+        wl = MI.small_workload(T, 6, 2, 256, 256, wf, af, 81, 0.5)
+        p = Problem(wl, experts_for_oracle=[])
+        ref = p.run_gpu()["out"]
+        out = torch.empty((T, wl.hidden), dtype=torch.int16, device="cuda")
+        M.run(p.dims, p.h_dev, p.l_dev, p.weights, p.scales, wl.top_k, out)
+        torch.cuda.synchronize()
+        outs.append((ref, out.cpu().numpy().view(np.uint16)))
+    for ref, got in outs:
+        assert np.array_equal(ref, got)
+
+
 def test_empty_batch_is_noop():
     import torch
 
