@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
@@ -191,6 +191,55 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
 moe_status moe_run(const moe_dims* dims, const void* hidden, int64_t num_tokens,
                    const float* router_logits, const void* weights, const void* scales,
                    int32_t top_k, void* out, hipStream_t stream);
+
+/* The routing step of the run calls alone, same kernels (flashinfer PR #4793,
+ * Walkthrough: the fused MoE consumes the router's selected experts and final
+ * scales; flashinfer PR #3738, Implementation Notes: the grouped GEMM's
+ * per-expert work map is computed on the device before the GEMMs).
+ *   router_logits:  device float [num_tokens, num_experts] (finite values)
+ *   ids:            device int32 [num_tokens, top_k] out: the k largest logits
+ *                   per token in descending order, equal logits by the smaller
+ *                   expert index
+ *   weights:        device float [num_tokens, top_k] out: softmax over the k
+ *                   selected logits, in the order of ids
+ *   expert_offsets: device int32 [num_experts + 1] out: first expanded row of
+ *                   each expert; expert_offsets[num_experts] = num_tokens*top_k
+ *   row_token:      device int32 [num_tokens*top_k] out: token of each
+ *                   expanded row (expert-major, then token, then slot)
+ *   slot_row:       device int32 [num_tokens, top_k] out: expanded row of each
+ *                   (token, slot)
+ *   workspace:      device buffer of at least moe_workspace_query bytes for
+ *                   the same dims, num_tokens and top_k; the routing scratch
+ *                   (per-chunk counts) and the GEMM work map are written to its
+ *                   chunk_counts, tiles and num_tiles regions (moe_ws_layout)
+ * The outputs may lie inside the workspace at the offsets moe_workspace_layout
+ * gives for them (where moe_run_ws puts them).  num_tokens = 0 returns MOE_OK
+ * without launching.  Errors as moe_run_ws. */
+moe_status moe_route(const moe_dims* dims, const float* router_logits, int64_t num_tokens,
+                     int32_t top_k, int32_t* ids, float* weights, int32_t* expert_offsets,
+                     int32_t* row_token, int32_t* slot_row, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/* The token quantisation step of the run calls alone, same kernels
+ * (flashinfer PR #3738, Implementation Notes: per-token activation scales
+ * computed while the routed rows are expanded; flashinfer PR #4793,
+ * Walkthrough: MXFP8 dispatch packing and the MXFP4 activation pack of the
+ * w4a4 mode).
+ *   hidden:       device bf16 bits [num_tokens, hidden]
+ *   codes:        device uint8 out: [num_tokens, hidden] E4M3 (FP8_TOKEN,
+ *                 MXFP8) or [num_tokens, hidden/2] E2M1 with element 2i in the
+ *                 low nibble (MXFP4)
+ *   scales:       device float [num_tokens] out: amax/448 (1.0 for an
+ *                 all-zero token) for FP8_TOKEN; 1.0 for the MX formats
+ *   block_scales: device uint8 [num_tokens, 16*ceil(hidden/512)] out: E8M0
+ *                 codes per 32 elements in the matrix-core order described
+ *                 at moe_ws_layout.tok_bscales (MXFP8, MXFP4); must be null
+ *                 for FP8_TOKEN
+ * BF16 activations have no quantisation step: MOE_ERR_UNSUPPORTED.
+ * num_tokens = 0 returns MOE_OK without launching. */
+moe_status moe_quantize_tokens(const moe_dims* dims, const void* hidden, int64_t num_tokens,
+                               void* codes, float* scales, void* block_scales,
+                               hipStream_t stream);
 
 /* Tile configurations of the grouped GEMMs.  A call picks one of
  * MOE_NUM_GEMM_CFG configurations (0: 16-row tiles, 1: 48/64-row tiles, 2:

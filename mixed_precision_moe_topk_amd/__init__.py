@@ -24,7 +24,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_weights_query", "moe_prepare_weights",
            "moe_unpack_weights", "moe_workspace_query", "moe_workspace_layout", "moe_run_ws",
-           "moe_run", "moe_tune_set", "moe_tune_clear", "moe_autotune", "moe_trace_enable",
+           "moe_run", "moe_route", "moe_quantize_tokens", "moe_tune_set", "moe_tune_clear", "moe_autotune", "moe_trace_enable",
            "moe_trace_read")
 STAGES = ("route", "quant", "gemm1", "requant", "gemm2", "finalize")
 
@@ -72,6 +72,8 @@ def lib():
             "moe_workspace_layout": [DP, I64, I32, ctypes.POINTER(WsLayout)],
             "moe_run_ws": [DP, P, I64, P, P, P, I32, P, P, SZ, P],
             "moe_run": [DP, P, I64, P, P, P, I32, P, P],
+            "moe_route": [DP, P, I64, I32, P, P, P, P, P, P, SZ, P],
+            "moe_quantize_tokens": [DP, P, I64, P, P, P, P],
             "moe_tune_set": [DP, I64, I32, I32],
             "moe_tune_clear": [],
             "moe_autotune": [DP, P, I64, P, P, P, I32, I32, ctypes.POINTER(I32),
@@ -168,6 +170,28 @@ def run(d: LayerDims, hidden, logits, weights, scales, top_k: int, out, stream=N
     T = int(hidden.shape[0])
     _check(lib().moe_run(ctypes.byref(d.c()), _ptr(hidden), T, _ptr(logits), _ptr(weights),
                          _ptr(scales), top_k, _ptr(out), _stream(stream)))
+
+
+def route(d: LayerDims, logits, top_k: int, ids, weights, expert_offsets, row_token,
+          slot_row, workspace, stream=None):
+    """The routing step alone.  logits: float32 cuda [T, E]; outputs int32/
+    float32 cuda: ids [T, k], weights [T, k], expert_offsets [E + 1],
+    row_token [T*k], slot_row [T, k]; workspace: uint8 cuda of
+    workspace_query bytes."""
+    T = int(logits.shape[0])
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().moe_route(ctypes.byref(d.c()), _ptr(logits), T, top_k, _ptr(ids), _ptr(weights),
+                           _ptr(expert_offsets), _ptr(row_token), _ptr(slot_row),
+                           _ptr(workspace), nbytes, _stream(stream)))
+
+
+def quantize_tokens(d: LayerDims, hidden, codes, scales, block_scales=None, stream=None):
+    """The token quantisation step alone.  hidden: bf16 bits cuda [T, H];
+    codes: uint8 cuda [T, H] (E4M3) or [T, H/2] (E2M1); scales: float32 cuda
+    [T]; block_scales: uint8 cuda [T, 16*ceil(H/512)] for the MX formats."""
+    T = int(hidden.shape[0])
+    _check(lib().moe_quantize_tokens(ctypes.byref(d.c()), _ptr(hidden), T, _ptr(codes),
+                                     _ptr(scales), _ptr(block_scales), _stream(stream)))
 
 
 NUM_GEMM_CFG = 3

@@ -590,6 +590,72 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
                      workspace, workspace_bytes, stream, -1);
 }
 
+moe_status moe_route(const moe_dims* dims, const float* router_logits, int64_t num_tokens,
+                     int32_t top_k, int32_t* ids, float* weights, int32_t* expert_offsets,
+                     int32_t* row_token, int32_t* slot_row, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  moe_ws_layout L;
+  MOE_TRY(layout_of(dims, num_tokens, top_k, &L));
+  if (num_tokens == 0) return ok();
+  if (!router_logits || !ids || !weights || !expert_offsets || !row_token || !slot_row ||
+      !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(router_logits) || !aligned16(ids) || !aligned16(weights) ||
+      !aligned16(expert_offsets) || !aligned16(row_token) || !aligned16(slot_row) ||
+      !aligned16(workspace))
+    return fail(MOE_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes,
+                L.total);
+  MOE_TRY(check_device());
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  moe::RouteParams rp;
+  rp.logits = router_logits;
+  rp.tokens = num_tokens;
+  rp.experts = dims->num_experts;
+  rp.top_k = top_k;
+  rp.ids = ids;
+  rp.weights = weights;
+  rp.chunk_counts = reinterpret_cast<int32_t*>(ws + L.chunk_counts);
+  rp.nchunks = (int32_t)cdiv(num_tokens, moe::kRouteChunkTokens);
+  rp.offsets = expert_offsets;
+  rp.row_token = row_token;
+  rp.slot_row = slot_row;
+  rp.tiles = reinterpret_cast<moe::Tile*>(ws + L.tiles);
+  rp.num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
+  rp.tile_m = L.tile_m;
+  MOE_TRY(hip_check(moe::launch_route(rp, stream), "route", stream));
+  return ok();
+}
+
+moe_status moe_quantize_tokens(const moe_dims* dims, const void* hidden, int64_t num_tokens,
+                               void* codes, float* scales, void* block_scales,
+                               hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  if (dims->afmt == MOE_A_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "BF16 activations are not quantised");
+  if (num_tokens < 0 || num_tokens > ((int64_t)1 << 26))
+    return fail(MOE_ERR_INVALID_ARG, "num_tokens %lld outside [0, 2^26]", (long long)num_tokens);
+  const bool mx = dims->afmt == MOE_A_MXFP8 || dims->afmt == MOE_A_MXFP4;
+  if (!mx && block_scales)
+    return fail(MOE_ERR_INVALID_ARG, "block_scales must be null for FP8_TOKEN activations");
+  if (num_tokens == 0) return ok();
+  if (!hidden || !codes || !scales || (mx && !block_scales))
+    return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(hidden) || !aligned16(codes) || !aligned16(scales) ||
+      (mx && !aligned16(block_scales)))
+    return fail(MOE_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  MOE_TRY(check_device());
+  const int mode = dims->afmt == MOE_A_MXFP4   ? moe::kQuantMxfp4
+                   : dims->afmt == MOE_A_MXFP8 ? moe::kQuantMxfp8
+                                               : moe::kQuantFp8Row;
+  MOE_TRY(hip_check(moe::launch_quant_tokens(static_cast<const uint16_t*>(hidden), num_tokens,
+                                             dims->hidden, mode, static_cast<uint8_t*>(codes),
+                                             scales, static_cast<uint8_t*>(block_scales), stream),
+                    "quantize tokens", stream));
+  return ok();
+}
+
 moe_status moe_tune_set(const moe_dims* dims, int64_t num_tokens, int32_t top_k,
                         int32_t gemm_cfg) {
   moe_ws_layout L;

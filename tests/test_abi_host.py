@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == set(M.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
 
 
 def _d(**kw):
@@ -183,3 +183,31 @@ def test_trace_modes(L):
         assert L.moe_trace_enable(mode) == 0
     assert L.moe_trace_enable(7) == 1
     assert L.moe_trace_enable(M.TRACE_OFF) == 0
+
+
+def test_stage_calls_reject_before_launch(L):
+    """moe_route and moe_quantize_tokens check their arguments on the host:
+    no device is touched for any of these cases."""
+    d = _d(num_experts=8, hidden=256, inter=512).c()
+    ok, bad = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1000 + 4)
+    big = 1 << 30
+    # T = 0: success without a launch, null pointers included
+    assert L.moe_route(ctypes.byref(d), None, 0, 2, None, None, None, None, None, None, 0,
+                       None) == 0
+    assert L.moe_quantize_tokens(ctypes.byref(d), None, 0, None, None, None, None) == 0
+    # null, misaligned, top_k out of range, workspace too small
+    assert L.moe_route(ctypes.byref(d), ok, 4, 2, ok, ok, None, ok, ok, ok, big, None) == 1
+    assert L.moe_route(ctypes.byref(d), ok, 4, 2, ok, bad, ok, ok, ok, ok, big, None) == 1
+    assert L.moe_route(ctypes.byref(d), ok, 4, 9, ok, ok, ok, ok, ok, ok, big, None) == 1
+    assert L.moe_route(ctypes.byref(d), ok, 4, 2, ok, ok, ok, ok, ok, ok, 64, None) == 3
+    assert b"workspace" in L.moe_last_error()
+    # FP8 per-token activations take no block scales; BF16 has no quantiser
+    assert L.moe_quantize_tokens(ctypes.byref(d), ok, 4, ok, ok, ok, None) == 1
+    assert L.moe_quantize_tokens(ctypes.byref(d), ok, 4, None, ok, None, None) == 1
+    assert L.moe_quantize_tokens(ctypes.byref(d), bad, 4, ok, ok, None, None) == 1
+    assert L.moe_quantize_tokens(ctypes.byref(d), ok, -1, ok, ok, None, None) == 1
+    bf = _d(num_experts=8, hidden=256, inter=512, afmt="bf16").c()
+    assert L.moe_quantize_tokens(ctypes.byref(bf), ok, 4, ok, ok, None, None) == 2
+    mx = _d(num_experts=8, hidden=256, inter=512, afmt="mxfp8").c()
+    assert L.moe_quantize_tokens(ctypes.byref(mx), ok, 4, ok, ok, None, None) == 1  # needs block scales
+    assert L.moe_quantize_tokens(ctypes.byref(mx), ok, 4, ok, ok, bad, None) == 1
