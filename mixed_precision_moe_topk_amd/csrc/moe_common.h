@@ -254,7 +254,7 @@ inline GemmCfg gemm_cfg(int i, int variant) {
     case 1: return variant == kMxfp4Bf16 ? GemmCfg{4, 1, 3, 2} : GemmCfg{4, 1, 4, 4};  // 48 x 128 / 64 x 256
     default:
       return variant == kMxfp4Bf16 ? GemmCfg{4, 2, 4, 4}    // 128 x 128
-             : variant == kMxfp4Mxfp8 ? GemmCfg{8, 2, 4, 8}  // 128 x 512
+             : variant == kMxfp4Mxfp8 ? GemmCfg{8, 2, 5, 8}  // 160 x 512
              : variant == kMxfp4Mxfp4 ? GemmCfg{8, 2, 5, 8}  // 160 x 512
              : variant == kMxfp4Fp8 ? GemmCfg{8, 2, 5, 8}    // 160 x 512
                                   : GemmCfg{8, 2, 4, 4};   // 128 x 256

@@ -502,15 +502,16 @@ __global__ __launch_bounds__(kWave * NW, MINB) void k_gemm_ab(GemmParams p) {
 }
 
 // ----------------------------------------------------------------------------
-// Direct-to-LDS grouped GEMM for MXFP4 x FP8, 160 x 512 block tiles (WM = 5).
+// Direct-to-LDS grouped GEMM for MXFP4 weights, 160 x 512 block tiles (WM = 5).
 // 8 waves (2 x 4), each 80 rows x 128 device columns (5 x 8 MFMA tiles), so
 // one K step reads 18 KB of operands from LDS per 40 MFMAs per wave (40%
 // less LDS traffic per MFMA than 64 x 64 wave tiles).  160-row tiles
 // let one tile hold an expert of up to 160 rows: a tile costs about the same
 // whether full or not (its weight stream dominates), so fewer tiles per
-// expert is what counts.  With MXFP8 activations the waves also need the
-// activation scales in registers, which 5 x 8 tiles leave no room for, so
-// that variant runs 128 x 512 tiles (4 x 8 per wave).
+// expert is what counts.  With MXFP8 activations the waves also hold
+// activation scales; that variant reads each subtile's A fragment and scale
+// just before its MFMAs (two live at a time instead of five), which keeps
+// the 5 x 8 wave tile within 256 registers.
 // Operands reach LDS by global_load_lds (16 bytes per lane, lane L of a wave
 // instruction lands at M0 + 16 L; an SALU write of M0 needs one wait state
 // before the load reads it), so no staging registers are needed:
@@ -680,33 +681,70 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
       for (int j = 0; j < WN; ++j) sx[j] = *reinterpret_cast<const uint32_t*>(ss + j * 256);
     }
     // MXFP8: A scale dword of subtile i (row lane%16, k-block lane/16), read
-    // per step next to its operands (held across a group it costs the
-    // registers this tile does not have)
+    // per step next to its operands
     const uint8_t* sa = lds + L::kAsOff + ((ks >> 2) & 1) * L::kAsSlot +
                         (16 * WM * wm + (lane & 15)) * 16 + 4 * (lane >> 4);
     v8i bop[WN];
-#pragma unroll
-    for (int j = 0; j < WN; ++j) {
-      const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
-      bop[j] = fp4_operand(b);
-    }
     const uint8_t* as = lds + L::kAOff + (S & 1) * L::kABuf + (wm * WM) * (NF * 1024) + lane * 16;
+    if constexpr (MXA && !A4) {
+      // MXFP8: LDS reads in MFMA order, the A fragment and scale of subtile
+      // 0 and the weight fragments first, then those of subtile i + 1 while
+      // the MFMAs of subtile i run.  Only two A fragments are live at a time, which
+      // leaves the registers for the activation scales in the 160-row tile.
+      // The reads are unconditional (subtiles past the tile end hold copies
+      // of its last row); only the MFMAs of such subtiles are skipped.
+      uint4 alo[2], ahi[2];
+      int axr[2];
+      auto read_a = [&](int i, int buf) __attribute__((always_inline)) {
+        alo[buf] = *reinterpret_cast<const uint4*>(as + i * 2048);
+        ahi[buf] = *reinterpret_cast<const uint4*>(as + i * 2048 + 1024);
+        axr[buf] = *reinterpret_cast<const int*>(sa + i * 256);
+      };
+      read_a(0, 0);
 #pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      if (cols && i < nvalid) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(as + i * (NF * 1024));
-        v8i aop;
-        if constexpr (A4) {
-          aop = fp4_operand(lo);
-        } else {
-          const uint4 hi = *reinterpret_cast<const uint4*>(as + i * 2048 + 1024);
-          aop = as_v8i(lo, hi);
+      for (int j = 0; j < WN; ++j) {
+        const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
+        bop[j] = fp4_operand(b);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        if (i + 1 < WM) read_a(i + 1, (i + 1) & 1);
+        if (cols && i < nvalid) {
+          const v8i aop = as_v8i(alo[i & 1], ahi[i & 1]);
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                aop, bop[j], acc[i][j], AF, 4, S, axr[i & 1], S, (int)sx[j]);
         }
-        const int ax = MXA ? *reinterpret_cast<const int*>(sa + i * 256) : 127;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // per-token E4M3 and E2M1 (W4A4) activations: the compiler's own order
+      // (all of the step's fragments read before the first MFMA) measured
+      // 2-3 % faster than the order above
 #pragma unroll
-        for (int j = 0; j < WN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              aop, bop[j], acc[i][j], AF, 4, MXA ? S : 0, ax, S, (int)sx[j]);
+      for (int j = 0; j < WN; ++j) {
+        const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
+        bop[j] = fp4_operand(b);
+      }
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        if (cols && i < nvalid) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(as + i * (NF * 1024));
+          v8i aop;
+          if constexpr (A4) {
+            aop = fp4_operand(lo);
+          } else {
+            const uint4 hi = *reinterpret_cast<const uint4*>(as + i * 2048 + 1024);
+            aop = as_v8i(lo, hi);
+          }
+          const int ax = MXA ? *reinterpret_cast<const int*>(sa + i * 256) : 127;
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                aop, bop[j], acc[i][j], AF, 4, MXA ? S : 0, ax, S, (int)sx[j]);
+        }
       }
     }
     // the loads of step ks+1 (A issued above, weights one step earlier) have
@@ -751,8 +789,8 @@ __global__ __launch_bounds__(dma::kNW * kWave, 1) void k_gemm_dma(GemmParams p) 
 template <int V, bool FC1>
 static hipError_t launch_v(int cfg, const GemmParams& p, int64_t blocks, hipStream_t st) {
   if (cfg == 1) k_gemm_lds<V, FC1, 4, 1, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p);
-  else if constexpr (scaled_fp4(V))  // 160 x 512; 128 x 512 with MXFP8 scales (registers)
-    k_gemm_dma<V, FC1, V == kMxfp4Mxfp8 ? 4 : 5><<<(unsigned)blocks, dma::kNW * kWave, 0, st>>>(p);
+  else if constexpr (scaled_fp4(V))  // 160 x 512
+    k_gemm_dma<V, FC1, 5><<<(unsigned)blocks, dma::kNW * kWave, 0, st>>>(p);
   else k_gemm_ab<V, FC1, 8, 2, 4, 4><<<(unsigned)blocks, 512, 0, st>>>(p);
   return hipGetLastError();
 }

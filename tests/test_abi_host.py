@@ -107,7 +107,7 @@ def test_workspace_layout_mxfp8(L):
     assert lay.fc2_bscales >= lay.tok_bscales + 4096 * 224
     assert lay.fc2_bscales + 4096 * 8 * 64 <= lay.total
     assert lay.fc2_codes + 4096 * 8 * 2048 <= lay.fc2_scales  # one byte per code
-    assert lay.tile_m == 128 and lay.gemm_cfg == 2
+    assert lay.tile_m == 160 and lay.gemm_cfg == 2
     # 384 columns: one partial group of 16 bytes per row
     lay = M.workspace_layout(_d(num_experts=8, hidden=384, inter=256, afmt="mxfp8"), 100, 2)
     assert lay.fc2_bscales - lay.tok_bscales >= 100 * 16

@@ -14,7 +14,7 @@ SMALL = [
     (70, 6, 3, 384, 256, "mxfp4", "fp8", 11, 0.0),    # 35 rows/expert -> 48-row tiles
     (70, 6, 3, 384, 256, "mxfp4", "bf16", 12, 0.0),
     (70, 6, 3, 384, 256, "int4", "fp8", 13, 0.0),
-    (300, 5, 2, 256, 384, "mxfp4", "fp8", 14, 0.0),   # 120 rows/expert -> 128-row tiles, tails
+    (300, 5, 2, 256, 384, "mxfp4", "fp8", 14, 0.0),   # 120 rows/expert -> 160-row tiles, tails
     (300, 5, 2, 256, 384, "int4", "fp8", 15, 2.0),
     (300, 5, 2, 256, 384, "mxfp4", "bf16", 16, 2.0),
     (400, 4, 2, 384, 384, "mxfp4", "fp8", 21, 0.0),   # 200 rows/expert, full + ragged tiles, N tail
@@ -28,8 +28,8 @@ SMALL = [
     # MXFP8 activations: every tile configuration, K not a multiple of 512
     # (a partial 4-step scale group), ragged row and N tails
     (70, 6, 3, 384, 256, "mxfp4", "mxfp8", 31, 0.0),  # 64-row tiles
-    (300, 5, 2, 256, 384, "mxfp4", "mxfp8", 32, 2.0), # 128-row tiles, tails
-    (400, 4, 2, 384, 640, "mxfp4", "mxfp8", 33, 1.0), # full + ragged 128-row tiles, N tail
+    (300, 5, 2, 256, 384, "mxfp4", "mxfp8", 32, 2.0), # 160-row tiles, tails
+    (400, 4, 2, 384, 640, "mxfp4", "mxfp8", 33, 1.0), # full + ragged 160-row tiles, N tail
     (9, 40, 4, 512, 128, "mxfp4", "mxfp8", 34, 0.0),  # 16-row tiles, empty experts
     (6, 1, 1, 8320, 4224, "mxfp4", "mxfp8", 35, 0.0), # long rows, 17 scale groups (last partial)
     # W4A4 (MXFP4 activations): every tile configuration, partial scale groups
