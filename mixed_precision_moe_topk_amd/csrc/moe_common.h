@@ -251,7 +251,9 @@ constexpr int kNumGemmCfg = 3;
 inline GemmCfg gemm_cfg(int i, int variant) {
   switch (i) {
     case 0: return GemmCfg{4, 1, 1, 4};                                        // 16 x 256
-    case 1: return variant == kMxfp4Bf16 ? GemmCfg{4, 1, 3, 2} : GemmCfg{4, 1, 4, 4};  // 48 x 128 / 64 x 256
+    case 1: return variant == kMxfp4Bf16 ? GemmCfg{4, 1, 3, 2}    // 48 x 128
+             : variant == kInt4Fp8 ? GemmCfg{8, 1, 4, 4}     // 64 x 512
+                                   : GemmCfg{4, 1, 4, 4};  // 64 x 256
     default:
       return variant == kMxfp4Bf16 ? GemmCfg{4, 2, 4, 4}    // 128 x 128
              : variant == kMxfp4Mxfp8 ? GemmCfg{8, 2, 5, 8}  // 160 x 512

@@ -40,8 +40,11 @@ __device__ __forceinline__ void interleave_schedule() {
 // A into two register staging sets, weights (pre-shuffled, straight into the
 // MFMA operand registers) into four register sets, so a load has two steps of
 // MFMA work to arrive.  An MXFP4 scale word covers four K steps (one E8M0 byte
-// per step), so it is loaded once per four steps.  Rows past the tile end are loaded as copies of its
-// last row and never stored; 16-row subtiles past the end are skipped.
+// per step), so it is loaded once per four steps; so are the INT4 group
+// scales (one float per lane covering four steps of a 16-column block, read
+// across lanes with ds_bpermute).  Rows past the tile end are loaded as
+// copies of its last row and never stored; 16-row subtiles past the end are
+// skipped.
 // Body of k_gemm_lds for one work item.  FULL: the tile has BM rows and the
 // wave's columns lie inside N (known per block), so every step is one basic
 // block: no per-subtile branches, which lets the scheduling hints interleave
@@ -134,8 +137,11 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
 
   v4u ast[AS][NCH];
   uint4 bq[NB][WN];
-  uint32_t sq[NB][WN];         // INT4 group scales, one set per B register set
-  uint32_t sx[WN], sx_next[WN];  // MXFP4 scale words of this / the next 4 steps
+  // MXFP4: E8M0 scale words of this / the next 4 steps.  INT4: lane L holds
+  // the float32 group scale of column L%16 at step 4g + L/16 of this / the
+  // next 4-step group g (the layout keeps those 64 floats contiguous); an
+  // MFMA lane takes its column's scale for step S from lane L%16 + 16 S.
+  uint32_t sx[WN], sx_next[WN];
   uint32_t ax[WM], ax_next[WM];  // MXFP8 A scale dwords of this / the next 4 steps
 
   auto load_a = [&](int ks, v4u (&dst)[NCH]) __attribute__((always_inline)) {
@@ -150,20 +156,23 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
   // column block (never used).  A branch around them would make the
   // compiler's wait counts assume they may be missing and drain the prefetch.
   const int64_t nb_last = p.N / 16 - 1;
-  auto load_b = [&](int ks, uint4 (&b)[WN], uint32_t (&sc)[WN]) __attribute__((always_inline)) {
+  auto load_b = [&](int ks, uint4 (&b)[WN]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
       const int64_t nb = min(nb0 + j, nb_last);
       b[j] = *reinterpret_cast<const uint4*>(wbase + ((nb * KS + ks) * 64 + lane) * 16);
-      if (!MX)
-        sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS + ks) * 16 + (lane & 15)) * 4);
     }
   };
   auto load_sx = [&](int ks, uint32_t (&sc)[WN]) __attribute__((always_inline)) {
+    // INT4: step 4g + L/16 of the group, clamped to the last step (unused)
+    const int64_t gstep = min(((ks >> 2) << 2) + (lane >> 4), KS - 1);
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
       const int64_t nb = min(nb0 + j, nb_last);
-      sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS4 + (ks >> 2)) * 64 + lane) * 4);
+      if constexpr (MX)
+        sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS4 + (ks >> 2)) * 64 + lane) * 4);
+      else
+        sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS + gstep) * 16 + (lane & 15)) * 4);
     }
     if constexpr (MXA) {
 #pragma unroll
@@ -179,7 +188,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
   auto step = [&](auto s_c, int ks) __attribute__((always_inline)) {
     constexpr int S = decltype(s_c)::value;
     // the scale words of steps ks..ks+3 were loaded PB steps ago
-    if constexpr (MX && S == 0) {
+    if constexpr (S == 0) {
 #pragma unroll
       for (int j = 0; j < WN; ++j) sx[j] = sx_next[j];
       if constexpr (MXA) {
@@ -188,8 +197,8 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
       }
     }
     load_a(min(ks + AD, KS - 1), ast[(S + AD) % AS]);
-    load_b(min(ks + PB, KS - 1), bq[(S + PB) % NB], sq[(S + PB) % NB]);
-    constexpr bool LOAD_SX = MX && (S + PB) % 4 == 0;
+    load_b(min(ks + PB, KS - 1), bq[(S + PB) % NB]);
+    constexpr bool LOAD_SX = (S + PB) % 4 == 0;
     if constexpr (LOAD_SX) load_sx(min(ks + PB, KS - 1), sx_next);
 #if !MOE_INTERLEAVE
     // keep the step's phases in order (prefetch | LDS reads + MFMAs | LDS
@@ -198,9 +207,13 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
 #endif
     const uint8_t* abuf = lds + (S & 1) * ABUF + (WM * wm) * (NF * 1024);
     v8i bop[WN];
+    float gs[WN];  // INT4: this step's group scale of the lane's column
 #pragma unroll
-    for (int j = 0; j < WN; ++j)
+    for (int j = 0; j < WN; ++j) {
       bop[j] = MX ? fp4_operand(bq[S % NB][j]) : int4_operand(bq[S % NB][j]);
+      if constexpr (!MX)
+        gs[j] = __uint_as_float(__builtin_amdgcn_ds_bpermute(((lane & 15) + 16 * S) << 2, (int)sx[j]));
+    }
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       if (FULL || (cols && i < nvalid)) {
@@ -220,9 +233,8 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
           } else {
             const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 aop, bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-            const float gs = __uint_as_float(sq[S % NB][j]);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[i][j][v] += part[v] * gs;
+            for (int v = 0; v < 4; ++v) acc[i][j][v] += part[v] * gs[j];
           }
         }
       }
@@ -230,7 +242,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
 #if MOE_INTERLEAVE
     // issue order inside the step: the wave's global loads and LDS reads are
     // spread between its MFMAs so they issue while the matrix pipe is busy
-    if (FULL) interleave_schedule<WM * WN, (MX ? (LOAD_SX ? 2 : 1) : 2) * WN + NCH + (LOAD_SX && MXA ? WM : 0), NF * WM>();
+    if (FULL) interleave_schedule<WM * WN, (LOAD_SX ? 2 : 1) * WN + NCH + (LOAD_SX && MXA ? WM : 0), NF * WM>();
 #endif
     __builtin_amdgcn_sched_barrier(0);
     // A of step ks+1 (a harmless copy of the last step once past the end)
@@ -243,8 +255,8 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
   // loop head are the minimum over the entry and back-edge paths, so a late
   // load here would tighten every iteration's waits.
   load_a(0, ast[0]);
-  load_b(0, bq[0], sq[0]);
-  if (MX) load_sx(0, sx_next);
+  load_b(0, bq[0]);
+  load_sx(0, sx_next);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 1; i < AD; ++i) {
@@ -253,7 +265,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
   }
 #pragma unroll
   for (int i = 1; i < PB; ++i) {
-    load_b(min(i, KS - 1), bq[i], sq[i]);
+    load_b(min(i, KS - 1), bq[i]);
     __builtin_amdgcn_sched_barrier(0);
   }
   store_a(0, ast[0]);
@@ -788,7 +800,12 @@ __global__ __launch_bounds__(dma::kNW * kWave, 1) void k_gemm_dma(GemmParams p) 
 
 template <int V, bool FC1>
 static hipError_t launch_v(int cfg, const GemmParams& p, int64_t blocks, hipStream_t st) {
-  if (cfg == 1) k_gemm_lds<V, FC1, 4, 1, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p);
+  if (cfg == 1) {
+    // INT4: 8 waves side by side over 512 columns, so each staged A tile
+    // serves twice the columns (GEMM1 10 % faster than 4 waves over 256)
+    if constexpr (V == kInt4Fp8) k_gemm_lds<V, FC1, 8, 1, 4, 4, 1><<<(unsigned)blocks, 512, 0, st>>>(p);
+    else k_gemm_lds<V, FC1, 4, 1, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p);
+  }
   else if constexpr (scaled_fp4(V))  // 160 x 512
     k_gemm_dma<V, FC1, 5><<<(unsigned)blocks, dma::kNW * kWave, 0, st>>>(p);
   else k_gemm_ab<V, FC1, 8, 2, 4, 4><<<(unsigned)blocks, 512, 0, st>>>(p);
