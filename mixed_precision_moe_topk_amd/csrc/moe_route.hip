@@ -16,25 +16,33 @@
 // grid indexes it with a 64-bit linear block index.
 #include "moe_common.h"
 
+// Wave-wide reductions of the ROCm device library (results in every lane).
+extern "C" __device__ __attribute__((const)) float __ockl_wfred_max_f32(float);
+extern "C" __device__ __attribute__((const)) int __ockl_wfred_min_i32(int);
+
 namespace moe {
 
 // Top-k and softmax of token t, by one wave.  Lane j holds logits j, j+64,
-// ... (E <= 1024).
+// ..., PER of them (E <= 64 PER).  Each of the k rounds takes every lane's
+// best remaining logit (larger value, then smaller expert index), the wave
+// maximum of those by a reduction, and the lanes that hold the maximum by a
+// ballot; if more than one lane holds it (an exact tie, or -0.0 against
+// +0.0), the smallest expert index among them wins, by a second reduction.
+// A round is thus a chain of two or three wave reductions instead of a
+// six-step shuffle of value and index.
+template <int PER>
 __device__ __forceinline__ void route_token(const RouteParams& p, const int64_t t) {
   const int lane = lane_id();
   const int E = p.experts;
   const float* row = p.logits + t * E;
-  constexpr int kPer = kMaxExperts / kWave;  // 16
-  float v[kPer];
+  float v[PER];
+  uint32_t taken = 0;  // bit i: value i of this lane already selected (or absent)
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
+  for (int i = 0; i < PER; ++i) {
     const int e = lane + i * kWave;
     v[i] = (e < E) ? row[e] : 0.0f;
+    if (e >= E) taken |= 1u << i;
   }
-  uint32_t taken = 0;  // bit i: value i of this lane already selected
-#pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    if (lane + i * kWave >= E) taken |= 1u << i;
 
   float sel_v[kMaxTopK];
   int sel_e[kMaxTopK];
@@ -45,31 +53,27 @@ __device__ __forceinline__ void route_token(const RouteParams& p, const int64_t 
     sel_e[j] = 0;
     if (j >= K) continue;
     // lane-local best: larger value, then smaller expert index
-    float bv = 0.0f;
+    float bv = -INFINITY;
     int be = 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = 0; i < PER; ++i) {
       if (taken & (1u << i)) continue;
-      const int e = lane + i * kWave;
       if (be == 0x7FFFFFFF || v[i] > bv) {  // indices grow with i: ties keep the first
         bv = v[i];
-        be = e;
+        be = lane + i * kWave;
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oe = __shfl_xor(be, o);
-      const bool better = (oe != 0x7FFFFFFF) &&
-                          (be == 0x7FFFFFFF || ov > bv || (ov == bv && oe < be));
-      if (better) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    sel_v[j] = bv;
-    sel_e[j] = be;
-    if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
+    const float vmax = __ockl_wfred_max_f32(bv);
+    const bool hold = be != 0x7FFFFFFF && bv == vmax;
+    const uint64_t holders = __ballot(hold);
+    int win;
+    if (__popcll(holders) == 1)
+      win = __builtin_amdgcn_readlane(be, __ffsll((unsigned long long)holders) - 1);
+    else
+      win = __ockl_wfred_min_i32(hold ? be : 0x7FFFFFFF);
+    sel_v[j] = vmax;
+    sel_e[j] = win;
+    if ((win & (kWave - 1)) == lane) taken |= 1u << (win / kWave);
   }
   // softmax over the selected logits (sel_v[0] is the largest)
   float sum = 0.0f;
@@ -89,9 +93,10 @@ __device__ __forceinline__ void route_token(const RouteParams& p, const int64_t 
 }
 
 // One wave per token.
+template <int PER>
 __global__ __launch_bounds__(256) void k_router(RouteParams p) {
   const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (t < p.tokens) route_token(p, t);
+  if (t < p.tokens) route_token<PER>(p, t);
 }
 
 // Routing index over chunks of kChunkTokens tokens (one wave per chunk).  For
@@ -238,7 +243,13 @@ __global__ __launch_bounds__(1024) void k_route_small(RouteParams p) {
 hipError_t launch_route(const RouteParams& p, hipStream_t st) {
   if (p.tokens == 0) return hipSuccess;
   const int wpb = 4;
-  k_router<<<(unsigned)((p.tokens + wpb - 1) / wpb), wpb * kWave, 0, st>>>(p);
+  const dim3 grid((unsigned)((p.tokens + wpb - 1) / wpb)), block(wpb * kWave);
+  // logits per lane: the fewest that hold all experts
+  if (p.experts <= 64) k_router<1><<<grid, block, 0, st>>>(p);
+  else if (p.experts <= 128) k_router<2><<<grid, block, 0, st>>>(p);
+  else if (p.experts <= 256) k_router<4><<<grid, block, 0, st>>>(p);
+  else if (p.experts <= 512) k_router<8><<<grid, block, 0, st>>>(p);
+  else k_router<16><<<grid, block, 0, st>>>(p);
   if (p.tokens <= kChunkTokens) {
     k_route_small<<<1, 1024, 0, st>>>(p);
     return hipGetLastError();
