@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef enum {
   MOE_OK = 0,
@@ -100,8 +100,8 @@ typedef struct {
  *                               when fc2_fused)
  *   fc2_codes   uint8  [T*k, I] E4M3 (FP8, MXFP8), [T*k, I/2] E2M1 (MXFP4) or
  *                               bf16 bits ([T*k, I] uint16)
- *   fc2_scales  float  [T*k]    per-row FC2 input scale (FP8; 1.0 for BF16; not
- *                               written for the MX formats)
+ *   fc2_scales  float  [T*k]    per-row FC2 input scale (FP8; not written for
+ *                               the MX formats and BF16)
  *   tok_bscales uint8  [T, 16*ceil(H/512)]   E8M0 block scales of the token
  *                                  codes (MXFP8, MXFP4), in matrix-core order:
  *                                  the scale of elements [32b, 32b + 32) of a
@@ -111,8 +111,8 @@ typedef struct {
  *   num_tiles   int32  [1]      GEMM work-map length; tile_m rows per tile
  * gemm_cfg is the tile configuration the call uses (tuned or default, see
  * moe_tune_set), max_tiles the bound on its work-map length.  fc2_fused = 1:
- * GEMM1 quantises its output to the FC2 input itself (MX activation formats),
- * so h is not written and fc2_scales are not set. */
+ * GEMM1 writes the FC2 input itself (MX activation formats: codes and block
+ * scales; BF16: bf16(h)), so h is not written and fc2_scales are not set. */
 typedef struct {
   size_t total;
   size_t ids, topk_w, chunk_counts, offsets, row_token, slot_row, tiles, num_tiles;

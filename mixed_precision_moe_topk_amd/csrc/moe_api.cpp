@@ -212,8 +212,10 @@ moe_status layout_of(const moe_dims* d, int64_t T, int32_t k, moe_ws_layout* L, 
   L->tile_m = tile_m;
   L->gemm_cfg = cfg;
   L->max_tiles = max_tiles;
-  // waves whose tiles hold whole 32-column blocks of h (4 column blocks)
-  L->fc2_fused = mx && moe::gemm_cfg(cfg, variant_of(d)).wn % 4 == 0;
+  // GEMM1 writes the FC2 input itself: MX formats on waves whose tiles hold
+  // whole 32-column blocks of h (4 column blocks), BF16 always (bf16(h) is
+  // element-wise)
+  L->fc2_fused = (mx && moe::gemm_cfg(cfg, variant_of(d)).wn % 4 == 0) || d->afmt == MOE_A_BF16;
   return MOE_OK;
 }
 
@@ -502,9 +504,9 @@ moe_status run_checked(const moe_dims* dims, const void* hidden, int64_t num_tok
   uint8_t* q2 = ws + L.fc2_codes;
   float* s2 = reinterpret_cast<float*>(ws + L.fc2_scales);
   uint8_t* b2 = mx ? ws + L.fc2_bscales : nullptr;
-  // MX formats: GEMM1 writes the FC2 input itself
+  // MX formats and BF16: GEMM1 writes the FC2 input itself
   g1.q_out = L.fc2_fused ? q2 : nullptr;
-  g1.q_stride = e2m1 ? I / 2 : I;
+  g1.q_stride = e2m1 ? I / 2 : (fp8 || mx) ? I : 2 * I;  // bytes per row
   g1.q_bscales = L.fc2_fused ? b2 : nullptr;
   g1.q_bstride = moe::mx_scale_row_bytes(I);
   MOE_TRY(hip_check(moe::launch_gemm(variant, true, L.gemm_cfg, g1, L.max_tiles, stream),

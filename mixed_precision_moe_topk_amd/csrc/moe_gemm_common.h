@@ -241,9 +241,38 @@ __device__ __forceinline__ void epilogue_fc1_mx(const GemmParams& p, const v4f (
   }
 }
 
-// End of a GEMM block: the fused FC1 + FC2-quantisation epilogue when the
-// caller asks for it (q_out set) and the format and tile allow it, else the
-// plain epilogue.
+// FC1 epilogue for BF16 activations: the FC2 input is bf16(h) element by
+// element (no row scale), so GEMM1 writes those bits (q_out, q_stride bytes
+// per row) in place of h: the same h value and rounding as the separate
+// conversion, without the float32 round trip.
+template <int WM, int WN>
+__device__ __forceinline__ void epilogue_fc1_bf16(const GemmParams& p, const v4f (&acc)[WM][WN],
+                                                  int row_base, int row_end, int nvalid,
+                                                  int64_t nb0, int jvalid, int lane) {
+  const int col_lane = lane & 15;
+  const int row_lane = 4 * (lane >> 4);
+#pragma unroll
+  for (int q = 0; q < WN / 2; ++q) {
+    if (2 * q >= jvalid) continue;
+    const int64_t c = ((nb0 + 2 * q) >> 1) * 16 + col_lane;
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      if (i >= nvalid) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = row_base + 16 * i + row_lane + v;
+        if (r < row_end) {
+          const float h = silu(acc[i][2 * q][v]) * acc[i][2 * q + 1][v];
+          reinterpret_cast<uint16_t*>(p.q_out + (int64_t)r * p.q_stride)[c] = (uint16_t)bf16_bits(h);
+        }
+      }
+    }
+  }
+}
+
+// End of a GEMM block: the fused FC1 + FC2-input epilogue when the caller
+// asks for it (q_out set) and the format and tile allow it, else the plain
+// epilogue.
 template <int V, bool FC1, int WM, int WN>
 __device__ __forceinline__ void finish_tile(const GemmParams& p, const v4f (&acc)[WM][WN],
                                             int row_base, int row_end, int nvalid, int64_t nb0,
@@ -251,6 +280,12 @@ __device__ __forceinline__ void finish_tile(const GemmParams& p, const v4f (&acc
   if constexpr (FC1 && a_blockscaled(V) && WN % 4 == 0) {
     if (p.q_out) {
       epilogue_fc1_mx<a_fp4(V), WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+      return;
+    }
+  }
+  if constexpr (FC1 && V == kMxfp4Bf16) {
+    if (p.q_out) {
+      epilogue_fc1_bf16<WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
       return;
     }
   }

@@ -198,5 +198,12 @@ def compare_all(g, r, wl, exact_rows=True):
         dq = dec(g["fc2_codes"], g["fc2_block_scales"])
         dr = dec(r["fc2_codes"], r["fc2_block_scales"])
         assert rel_l2(dq, dr) <= 1e-3
+    if wl.afmt == "bf16":
+        # FC2 input bf16(h) (written by GEMM1's epilogue): h differs from the
+        # oracle's by float32 rounding, so a few values round to the
+        # neighbouring bf16
+        same = np.mean(g["fc2_codes"] == r["fc2_codes"])
+        assert same > 0.97, same
+        assert rel_l2(F.bf16_to_f32(g["fc2_codes"]), F.bf16_to_f32(r["fc2_codes"])) <= 1e-3
     assert rel_l2(g["y2"], r["y2"]) <= 2e-3, rel_l2(g["y2"], r["y2"])
     return check_output(g["out"], r["out"])

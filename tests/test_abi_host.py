@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == set(M.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 5
+    assert L.moe_abi_version() == 6
 
 
 def _d(**kw):
@@ -170,11 +170,11 @@ def test_workspace_layout_w4a4(L):
     assert a.total < b.total
     assert a.fc2_bscales - a.tok_bscales == b.fc2_bscales - b.tok_bscales
     assert a.tile_m == 160 and a.gemm_cfg == 2
-    # GEMM1 quantises the FC2 input itself for the MX formats only
+    # GEMM1 writes the FC2 input itself for the MX formats and BF16, not for per-token FP8
     assert a.fc2_fused == 1 and b.fc2_fused == 1
     assert M.workspace_layout(_d(afmt="mxfp4"), 64, 8).fc2_fused == 1
     assert M.workspace_layout(_d(), 4096, 8).fc2_fused == 0
-    assert M.workspace_layout(_d(afmt="bf16"), 64, 8).fc2_fused == 0
+    assert M.workspace_layout(_d(afmt="bf16"), 64, 8).fc2_fused == 1  # bf16(h) from GEMM1
 
 
 def test_trace_modes(L):
