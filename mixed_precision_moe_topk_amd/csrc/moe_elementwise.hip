@@ -221,9 +221,10 @@ __global__ __launch_bounds__(256) void k_quant_mx(const void* __restrict__ src, 
   if (threadIdx.x == 0) scales[r] = 1.0f;
 }
 
-// One block per token: out[t] = bf16(sum_j fl32(w[t,j] * y2[row(t,j)])), the
-// float32 sum taken in slot order.  H % 4 == 0.  The block walks its k rows
-// from start to end, so each row is read as one sequential stream.  KC > 0: top-k known at
+// Blocks (t, y): out[t] = bf16(sum_j fl32(w[t,j] * y2[row(t,j)])), the float32
+// sum taken in slot order, over the float4 columns y, y + gridDim.y, ... (in
+// units of 256).  H % 4 == 0.  A block walks its k rows from start to end, so
+// each row is read as one sequential stream.  KC > 0: top-k known at
 // compile time, so the k row loads of a column group are issued together
 // (one load in flight per thread would leave the kernel latency-bound).
 template <int KC>
@@ -235,7 +236,8 @@ __global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ y2,
   const int64_t t = blockIdx.x;
   const int k = KC > 0 ? KC : k_rt;
   const int nv = H / 4;
-  for (int i = threadIdx.x; i < nv; i += blockDim.x) {
+  // blockIdx.y splits the token's columns when there are few tokens
+  for (int i = blockIdx.y * blockDim.x + threadIdx.x; i < nv; i += gridDim.y * blockDim.x) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if constexpr (KC > 0) {
       float4 y[KC];
@@ -291,7 +293,12 @@ hipError_t launch_finalize(const float* y2, const float* weights, const int32_t*
                            int64_t T, int32_t k, int32_t H, uint16_t* out, hipStream_t st) {
   if (T == 0) return hipSuccess;
   // one block per token, walking its k rows from start to end
-  const dim3 grid((unsigned)T);
+  // a block of 256 threads walks a token's H/4 float4 columns; with few
+  // tokens the columns are split over up to 2048 / T blocks per token so that
+  // a small batch still fills the GPU (64 tokens, H = 7168: 7 blocks each)
+  const int64_t nchunk = (H / 4 + 255) / 256;
+  const int64_t split = std::max<int64_t>(1, std::min<int64_t>(nchunk, 2048 / std::max<int64_t>(T, 1)));
+  const dim3 grid((unsigned)T, (unsigned)split);
   switch (k) {
     case 2: k_finalize<2><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
     case 4: k_finalize<4><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
