@@ -292,7 +292,6 @@ hipError_t launch_requant(const float* h, int64_t rows, int32_t I, int mode, uin
 hipError_t launch_finalize(const float* y2, const float* weights, const int32_t* slot_row,
                            int64_t T, int32_t k, int32_t H, uint16_t* out, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  // one block per token, walking its k rows from start to end
   // a block of 256 threads walks a token's H/4 float4 columns; with few
   // tokens the columns are split over up to 2048 / T blocks per token so that
   // a small batch still fills the GPU (64 tokens, H = 7168: 7 blocks each)
