@@ -651,6 +651,13 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
 #pragma unroll
     for (int u = 0; u < kBPW; ++u) lds_dma16_s(wcol[u] + ks * 1024, lane * 16, dst + u * 1024);
   };
+  // half h (0 or 1) of issue_b's loads
+  auto issue_b_part = [&](int ks, int stage, int h) __attribute__((always_inline)) {
+    const uint32_t dst = lds0 + L::kBOff + stage * kBBuf + wave * kBPW * 1024;
+#pragma unroll
+    for (int u = h * (kBPW / 2); u < (h + 1) * (kBPW / 2); ++u)
+      lds_dma16_s(wcol[u] + ks * 1024, lane * 16, dst + u * 1024);
+  };
   // MXFP8: wave w < L::kAsDma loads the activation-scale group of tile rows
   // 64 w + L (the last row repeated past the end); a 32-bit offset from the
   // scale array (its size is checked on the host) saves a register pair
@@ -682,10 +689,25 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   // weights (kBPW) and, at the start of a group, the scale words (kBPW)
   auto step = [&](auto s_c, int ks, int bstage) __attribute__((always_inline)) {
     constexpr int S = decltype(s_c)::value;
-    if constexpr (MXA && S == 0) issue_as(min((ks >> 2) + 1, KS4 - 1), ((ks >> 2) + 1) & 1);
-    issue_a(min(ks + 1, KS - 1), (S + 1) & 1);
-    issue_b(min(ks + 2, KS - 1), bstage == 0 ? 2 : bstage - 1);
-    if constexpr (S == 0) issue_sx(min((ks >> 2) + 1, KS4 - 1), ((ks >> 2) + 1) & 1);
+    // The step's direct-to-LDS loads are issued in four parts between the
+    // MFMA groups of subtiles 0-3, in the order activation scales, A,
+    // weights, scale words (the wait below relies on it).  Issued all at the
+    // top of the step, the eight waves' ~100 loads per CU queued in the
+    // address unit, and each wave's fragment reads and MFMAs waited behind
+    // its own loads (1,100-2,000 cycles per step, measured with s_memtime).
+    const int bnext = bstage == 0 ? 2 : bstage - 1;
+    auto issue_part = [&](int part) __attribute__((always_inline)) {
+      if (part == 0) {
+        if constexpr (MXA && S == 0) issue_as(min((ks >> 2) + 1, KS4 - 1), ((ks >> 2) + 1) & 1);
+        issue_a(min(ks + 1, KS - 1), (S + 1) & 1);
+      } else if (part == 1) {
+        issue_b_part(min(ks + 2, KS - 1), bnext, 0);
+      } else if (part == 2) {
+        issue_b_part(min(ks + 2, KS - 1), bnext, 1);
+      } else if (part == 3) {
+        if constexpr (S == 0) issue_sx(min((ks >> 2) + 1, KS4 - 1), ((ks >> 2) + 1) & 1);
+      }
+    };
     const uint8_t* bs = lds + L::kBOff + bstage * kBBuf + (wn * WN) * 1024 + lane * 16;
     if constexpr (S == 0) {
       const uint8_t* ss = lds + L::kSOff + ((ks >> 2) & 1) * kSxSlot + (wn * WN) * 256 + lane * 4;
@@ -730,6 +752,8 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
                 aop, bop[j], acc[i][j], AF, 4, S, axr[i & 1], S, (int)sx[j]);
         }
         __builtin_amdgcn_sched_barrier(0);
+        issue_part(i);
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
       // per-token E4M3 and E2M1 (W4A4) activations: the compiler's own order
@@ -757,8 +781,14 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 aop, bop[j], acc[i][j], AF, 4, MXA ? S : 0, ax, S, (int)sx[j]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        issue_part(i);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // subtiles fewer than the four load parts
+#pragma unroll
+    for (int part = WM; part < 4; ++part) issue_part(part);
     // the loads of step ks+1 (A issued above, weights one step earlier) have
     // landed once only the loads issued after this step's A loads remain
     wait_barrier<(S == 0 ? 2 * kBPW : kBPW)>();
