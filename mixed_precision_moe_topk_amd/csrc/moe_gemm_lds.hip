@@ -600,6 +600,10 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   constexpr int WN = kWN;
   using L = Map<WM, MXA, A4>;
   constexpr int NF = L::kNF;
+  // MXFP8 FC2 inputs: the step order pipelined across the barrier (15 %
+  // faster on the 4096-token DeepSeek-V3 GEMM2; 2-4 % slower than the orders
+  // below on GEMM1 and with per-token E4M3 activations, same-box A/B)
+  constexpr bool PIPE = MXA && !A4 && !FC1;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = lane_id();
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int row_end = tile.row0 + tile.nrows;
@@ -684,6 +688,32 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   uint32_t sx[WN];
+  uint4 bq[WN];          // weight fragments (the E2M1 operand is built at each MFMA)
+  uint4 alo[2], ahi[2];  // A fragment halves, two subtiles in flight
+  int axr[2];            // MXFP8: the A scale dwords of those subtiles
+
+  // LDS addresses of this lane's fragments: weights of B stage bst, A of
+  // A stage ast, weight scale words and MXFP8 A scales of step ksx's group
+  auto b_at = [&](int bst) __attribute__((always_inline)) {
+    return lds + L::kBOff + bst * kBBuf + (wn * WN) * 1024 + lane * 16;
+  };
+  auto a_at = [&](int ast) __attribute__((always_inline)) {
+    return lds + L::kAOff + ast * L::kABuf + (wm * WM) * (NF * 1024) + lane * 16;
+  };
+  auto sx_at = [&](int ksx) __attribute__((always_inline)) {
+    return lds + L::kSOff + ((ksx >> 2) & 1) * kSxSlot + (wn * WN) * 256 + lane * 4;
+  };
+  // MXFP8: A scale dword of subtile i is at + 256 i (row lane%16, k-block lane/16)
+  auto sa_at = [&](int ksx) __attribute__((always_inline)) {
+    return lds + L::kAsOff + ((ksx >> 2) & 1) * L::kAsSlot + (16 * WM * wm + (lane & 15)) * 16 +
+           4 * (lane >> 4);
+  };
+  auto read_a = [&](const uint8_t* as, const uint8_t* sa, int i, int buf)
+                    __attribute__((always_inline)) {
+    alo[buf] = *reinterpret_cast<const uint4*>(as + i * 2048);
+    ahi[buf] = *reinterpret_cast<const uint4*>(as + i * 2048 + 1024);
+    if constexpr (MXA) axr[buf] = *reinterpret_cast<const int*>(sa + i * 256);
+  };
 
   // loads per step after the A loads (which come first, 2 or 4 per wave):
   // weights (kBPW) and, at the start of a group, the scale words (kBPW)
@@ -708,90 +738,133 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
         if constexpr (S == 0) issue_sx(min((ks >> 2) + 1, KS4 - 1), ((ks >> 2) + 1) & 1);
       }
     };
-    const uint8_t* bs = lds + L::kBOff + bstage * kBBuf + (wn * WN) * 1024 + lane * 16;
-    if constexpr (S == 0) {
-      const uint8_t* ss = lds + L::kSOff + ((ks >> 2) & 1) * kSxSlot + (wn * WN) * 256 + lane * 4;
+    if constexpr (PIPE) {
+      // MXFP8 FC2 inputs, software-pipelined across the barrier:
+      // the step enters with its weight fragments, scale words and the A
+      // fragment of subtile 0 already in registers; subtile i + 1 is read
+      // while the MFMAs of subtile i run; the barrier that publishes the next
+      // step's tiles sits before the last subtile, whose MFMAs then each
+      // give way to the read of one of the next step's weight fragments.
+      // Placed after the last subtile, the barrier left each SIMD's matrix
+      // pipe idle until the eight waves' fragment reads had all come back.
+      constexpr int P0 = (S * WM) & 1;  // A register buffer of subtile 0
+      const uint8_t* as = a_at(S & 1);
+      const uint8_t* sa = sa_at(ks);
 #pragma unroll
-      for (int j = 0; j < WN; ++j) sx[j] = *reinterpret_cast<const uint32_t*>(ss + j * 256);
-    }
-    // MXFP8: A scale dword of subtile i (row lane%16, k-block lane/16), read
-    // per step next to its operands
-    const uint8_t* sa = lds + L::kAsOff + ((ks >> 2) & 1) * L::kAsSlot +
-                        (16 * WM * wm + (lane & 15)) * 16 + 4 * (lane >> 4);
-    v8i bop[WN];
-    const uint8_t* as = lds + L::kAOff + (S & 1) * L::kABuf + (wm * WM) * (NF * 1024) + lane * 16;
-    if constexpr (MXA && !A4) {
-      // MXFP8: LDS reads in MFMA order, the A fragment and scale of subtile
-      // 0 and the weight fragments first, then those of subtile i + 1 while
-      // the MFMAs of subtile i run.  Only two A fragments are live at a time, which
-      // leaves the registers for the activation scales in the 160-row tile.
-      // The reads are unconditional (subtiles past the tile end hold copies
-      // of its last row); only the MFMAs of such subtiles are skipped.
-      uint4 alo[2], ahi[2];
-      int axr[2];
-      auto read_a = [&](int i, int buf) __attribute__((always_inline)) {
-        alo[buf] = *reinterpret_cast<const uint4*>(as + i * 2048);
-        ahi[buf] = *reinterpret_cast<const uint4*>(as + i * 2048 + 1024);
-        axr[buf] = *reinterpret_cast<const int*>(sa + i * 256);
-      };
-      read_a(0, 0);
-#pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
-        bop[j] = fp4_operand(b);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < WM; ++i) {
-        if (i + 1 < WM) read_a(i + 1, (i + 1) & 1);
+      for (int i = 0; i + 1 < WM; ++i) {
+        read_a(as, sa, i + 1, (P0 + i + 1) & 1);
         if (cols && i < nvalid) {
-          const v8i aop = as_v8i(alo[i & 1], ahi[i & 1]);
+          const v8i aop = as_v8i(alo[(P0 + i) & 1], ahi[(P0 + i) & 1]);
+          const int ax = MXA ? axr[(P0 + i) & 1] : 127;
 #pragma unroll
           for (int j = 0; j < WN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                aop, bop[j], acc[i][j], AF, 4, S, axr[i & 1], S, (int)sx[j]);
+                aop, fp4_operand(bq[j]), acc[i][j], AF, 4, MXA ? S : 0, ax, S, (int)sx[j]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        issue_part(i);
+        if (i < 4) issue_part(i);
         __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int part = WM - 1; part < 4; ++part) issue_part(part);
+      wait_barrier<(S == 0 ? 2 * kBPW : kBPW)>();
+      // The reads below take the next step's tiles (past the last step they
+      // read LDS whose contents are never used).
+      constexpr int IL = WM - 1;
+      const uint8_t* bn = b_at(bstage == 2 ? 0 : bstage + 1);
+      const uint8_t* sn = sx_at(ks + 1);
+      const v8i aop = as_v8i(alo[(P0 + IL) & 1], ahi[(P0 + IL) & 1]);
+      const int ax = MXA ? axr[(P0 + IL) & 1] : 127;
+      const bool last = cols && IL < nvalid;
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        if (last)
+          acc[IL][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              aop, fp4_operand(bq[j]), acc[IL][j], AF, 4, MXA ? S : 0, ax, S, (int)sx[j]);
+        bq[j] = *reinterpret_cast<const uint4*>(bn + j * 1024);
+        if constexpr (S == 3) sx[j] = *reinterpret_cast<const uint32_t*>(sn + j * 256);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      read_a(a_at((S + 1) & 1), sa_at(ks + 1), 0, (P0 + WM) & 1);
     } else {
-      // per-token E4M3 and E2M1 (W4A4) activations: the compiler's own order
-      // (all of the step's fragments read before the first MFMA) measured
-      // 2-3 % faster than the order above
+      // all of the step's weight fragments are read after the barrier that
+      // ends the previous step
+      const uint8_t* bs = b_at(bstage);
+      if constexpr (S == 0) {
+        const uint8_t* ss = sx_at(ks);
 #pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
-        bop[j] = fp4_operand(b);
+        for (int j = 0; j < WN; ++j) sx[j] = *reinterpret_cast<const uint32_t*>(ss + j * 256);
       }
+      const uint8_t* sa = sa_at(ks);
+      const uint8_t* as = a_at(S & 1);
+      v8i bop[WN];
+      if constexpr (MXA && !A4) {
+        // MXFP8 GEMM1: LDS reads in MFMA order, the A fragment and scale of
+        // subtile 0 and the weight fragments first, then those of subtile
+        // i + 1 while the MFMAs of subtile i run.  Only two A fragments are
+        // live at a time, which leaves the registers for the activation
+        // scales in the 160-row tile.  The reads are unconditional
+        // (subtiles past the tile end hold copies of its last row); only the
+        // MFMAs of such subtiles are skipped.
+        read_a(as, sa, 0, 0);
 #pragma unroll
-      for (int i = 0; i < WM; ++i) {
-        if (cols && i < nvalid) {
-          const uint4 lo = *reinterpret_cast<const uint4*>(as + i * (NF * 1024));
-          v8i aop;
-          if constexpr (A4) {
-            aop = fp4_operand(lo);
-          } else {
-            const uint4 hi = *reinterpret_cast<const uint4*>(as + i * 2048 + 1024);
-            aop = as_v8i(lo, hi);
-          }
-          const int ax = MXA ? *reinterpret_cast<const int*>(sa + i * 256) : 127;
-#pragma unroll
-          for (int j = 0; j < WN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                aop, bop[j], acc[i][j], AF, 4, MXA ? S : 0, ax, S, (int)sx[j]);
+        for (int j = 0; j < WN; ++j) {
+          const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
+          bop[j] = fp4_operand(b);
         }
         __builtin_amdgcn_sched_barrier(0);
-        issue_part(i);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // subtiles fewer than the four load parts
 #pragma unroll
-    for (int part = WM; part < 4; ++part) issue_part(part);
-    // the loads of step ks+1 (A issued above, weights one step earlier) have
-    // landed once only the loads issued after this step's A loads remain
-    wait_barrier<(S == 0 ? 2 * kBPW : kBPW)>();
+        for (int i = 0; i < WM; ++i) {
+          if (i + 1 < WM) read_a(as, sa, i + 1, (i + 1) & 1);
+          if (cols && i < nvalid) {
+            const v8i aop = as_v8i(alo[i & 1], ahi[i & 1]);
+#pragma unroll
+            for (int j = 0; j < WN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  aop, bop[j], acc[i][j], AF, 4, S, axr[i & 1], S, (int)sx[j]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          issue_part(i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        // per-token E4M3 and E2M1 (W4A4) activations: the compiler's own
+        // order (all of the step's fragments read before the first MFMA)
+        // measured 2-3 % faster than the order above
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
+          bop[j] = fp4_operand(b);
+        }
+#pragma unroll
+        for (int i = 0; i < WM; ++i) {
+          if (cols && i < nvalid) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(as + i * (NF * 1024));
+            v8i aop;
+            if constexpr (A4) {
+              aop = fp4_operand(lo);
+            } else {
+              const uint4 hi = *reinterpret_cast<const uint4*>(as + i * 2048 + 1024);
+              aop = as_v8i(lo, hi);
+            }
+            const int ax = MXA ? *reinterpret_cast<const int*>(sa + i * 256) : 127;
+#pragma unroll
+            for (int j = 0; j < WN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  aop, bop[j], acc[i][j], AF, 4, MXA ? S : 0, ax, S, (int)sx[j]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          issue_part(i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // subtiles fewer than the four load parts
+#pragma unroll
+      for (int part = WM; part < 4; ++part) issue_part(part);
+      // the loads of step ks+1 (A issued above, weights one step earlier) have
+      // landed once only the loads issued after this step's A loads remain
+      wait_barrier<(S == 0 ? 2 * kBPW : kBPW)>();
+    }
   };
 
   // prologue: A and weights (and scales) of step 0, weights of step 1
@@ -801,6 +874,16 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   issue_sx(0, 0);
   issue_b(min(1, KS - 1), 1);
   wait_barrier<kBPW>();
+  if constexpr (PIPE) {
+    const uint8_t* b0 = b_at(0);
+    const uint8_t* s0 = sx_at(0);
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      bq[j] = *reinterpret_cast<const uint4*>(b0 + j * 1024);
+      sx[j] = *reinterpret_cast<const uint32_t*>(s0 + j * 256);
+    }
+    read_a(a_at(0), sa_at(0), 0, 0);
+  }
   int ks = 0, bstage = 0;
   for (; ks + 4 <= KS; ks += 4) {
     step(std::integral_constant<int, 0>{}, ks, bstage);
