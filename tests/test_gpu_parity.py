@@ -25,6 +25,7 @@ SMALL = [
     (1, 3, 3, 128, 128, "mxfp4", "fp8", 20, 0.0),     # single token, k = E
     (40, 1024, 16, 128, 128, "mxfp4", "fp8", 24, 0.0),  # the most experts and the largest top-k
     (6, 1, 1, 8320, 4224, "mxfp4", "fp8", 23, 0.0),   # rows longer than the quantisers keep in registers
+    (70, 6, 2, 256, 3072, "int4", "fp8", 25, 0.0),   # FC2 rows of 2048-4096 columns (requant, 16 float4 per lane)
     # MXFP8 activations: every tile configuration, K not a multiple of 512
     # (a partial 4-step scale group), ragged row and N tails
     (70, 6, 3, 384, 256, "mxfp4", "mxfp8", 31, 0.0),  # 64-row tiles
