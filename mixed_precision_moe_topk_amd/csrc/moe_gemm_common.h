@@ -128,17 +128,14 @@ __device__ __forceinline__ float silu(float g) {
 // read once, by the next kernel, long after the block is gone, and keeping
 // them out of the caches measured 1-4 % faster on the prefill GEMM2 and
 // finalize (an L2-resident y2 for a fused finalize by float atomics, tried
-// as well, made GEMM2 2.1x slower).
-template <bool FC1, int WM, int WN>
-__device__ __forceinline__ void epilogue(const GemmParams& p, const v4f (&acc)[WM][WN],
-                                         int row_base, int row_end, int nvalid, int64_t nb0,
-                                         int jvalid, int lane) {
-  const int col_lane = lane & 15;
+// as well, made GEMM2 2.1x slower).  epilogue_sc takes the row scales
+// loaded beforehand (load_row_scales), epilogue loads them itself.
+
+// Row scales of this lane's accumulator rows (1 without row scales).
+template <bool FC1, int WM>
+__device__ __forceinline__ void load_row_scales(const GemmParams& p, int row_base, int row_end,
+                                                int lane, float (&sc)[WM][4]) {
   const int row_lane = 4 * (lane >> 4);
-  // row scales of this lane's rows, loaded once before any store (the output
-  // may alias the scale arrays as far as the compiler knows, so loads placed
-  // between stores would each wait for the store before them)
-  float sc[WM][4];
 #pragma unroll
   for (int i = 0; i < WM; ++i)
 #pragma unroll
@@ -148,6 +145,14 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const v4f (&acc)[W
                  : FC1       ? p.row_scale[p.row_token[r]]
                              : p.row_scale[r];
     }
+}
+
+template <bool FC1, int WM, int WN>
+__device__ __forceinline__ void epilogue_sc(const GemmParams& p, const v4f (&acc)[WM][WN],
+                                            const float (&sc)[WM][4], int row_base, int row_end,
+                                            int nvalid, int64_t nb0, int jvalid, int lane) {
+  const int col_lane = lane & 15;
+  const int row_lane = 4 * (lane >> 4);
   if (FC1) {
 #pragma unroll
     for (int q = 0; q < WN / 2; ++q) {
@@ -185,6 +190,18 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const v4f (&acc)[W
       }
     }
   }
+}
+
+// Row scales loaded once before any store (the output may alias the scale
+// arrays as far as the compiler knows, so loads placed between stores would
+// each wait for the store before them).
+template <bool FC1, int WM, int WN>
+__device__ __forceinline__ void epilogue(const GemmParams& p, const v4f (&acc)[WM][WN],
+                                         int row_base, int row_end, int nvalid, int64_t nb0,
+                                         int jvalid, int lane) {
+  float sc[WM][4];
+  load_row_scales<FC1, WM>(p, row_base, row_end, lane, sc);
+  epilogue_sc<FC1, WM, WN>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
 // FC1 epilogue for MX activation formats that quantises the FC2 input in

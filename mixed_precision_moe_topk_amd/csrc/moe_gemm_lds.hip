@@ -687,6 +687,11 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   for (int i = 0; i < WM; ++i)
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // per-token E4M3: the row scales are loaded before the K loop, so their
+  // latency (two dependent loads through row_token for GEMM1) is not paid
+  // between the last MFMA and the first output store
+  float sc[WM][4];
+  if constexpr (!MXA) load_row_scales<FC1, WM>(p, row_base, row_end, lane, sc);
   uint32_t sx[WN];
   uint4 bq[WN];          // weight fragments (the E2M1 operand is built at each MFMA)
   uint4 alo[2], ahi[2];  // A fragment halves, two subtiles in flight
@@ -899,7 +904,10 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   if (ks + 1 < KS) { step(std::integral_constant<int, 1>{}, ks + 1, bstage); bstage = bstage == 2 ? 0 : bstage + 1; }
   if (ks + 2 < KS) step(std::integral_constant<int, 2>{}, ks + 2, bstage);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  finish_tile<V, FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  if constexpr (!MXA)
+    epilogue_sc<FC1, WM, WN>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  else
+    finish_tile<V, FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
 template <int V, bool FC1, int WM>
