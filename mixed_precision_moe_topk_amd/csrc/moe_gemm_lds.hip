@@ -134,6 +134,11 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
   for (int i = 0; i < WM; ++i)
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // per-token E4M3: row scales loaded before the K loop (their latency is
+  // then not paid between the last MFMA and the first output store)
+  constexpr bool PRE_SC = V == kMxfp4Fp8 || V == kInt4Fp8;
+  float sc[WM][4];
+  if constexpr (PRE_SC) load_row_scales<FC1, WM>(p, row_base, row_end, lane, sc);
 
   v4u ast[AS][NCH];
   uint4 bq[NB][WN];
@@ -280,7 +285,10 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
   if (ks < KS) step(std::integral_constant<int, 0>{}, ks);
   if (ks + 1 < KS) step(std::integral_constant<int, 1>{}, ks + 1);
   if (ks + 2 < KS) step(std::integral_constant<int, 2>{}, ks + 2);
-  finish_tile<V, FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  if constexpr (PRE_SC)
+    epilogue_sc<FC1, WM, WN>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  else
+    finish_tile<V, FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
 template <int V, bool FC1, int NW, int WAVES_M, int WM, int WN, int MINB = 2, int PB = 2,
