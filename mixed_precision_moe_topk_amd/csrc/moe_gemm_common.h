@@ -120,7 +120,9 @@ __device__ __forceinline__ float silu(float g) {
 }
 
 // Epilogue shared by the GEMM kernels.  Output tile (i, j) of a wave holds, in
-// lane l, column 16*(nb0+j) + l%16 of rows row_base + 16*i + 4*(l/16) + [0, 4).
+// lane l, column 16*(nb0+j) + l%16 of rows row_base + RS*i + 4*(l/16) + [0, 4)
+// (RS = 16: the wave's subtiles are consecutive 16-row groups; 32: every
+// second group).
 //   FC1: tiles (2q, 2q+1) are the gate and up halves of intermediate block
 //        (nb0 + 2q)/2; h = silu(g*s) * (u*s), s = token scale.
 //   FC2: y2 = acc * s, s = row scale.
@@ -132,7 +134,7 @@ __device__ __forceinline__ float silu(float g) {
 // loaded beforehand (load_row_scales), epilogue loads them itself.
 
 // Row scales of this lane's accumulator rows (1 without row scales).
-template <bool FC1, int WM>
+template <bool FC1, int WM, int RS = 16>
 __device__ __forceinline__ void load_row_scales(const GemmParams& p, int row_base, int row_end,
                                                 int lane, float (&sc)[WM][4]) {
   const int row_lane = 4 * (lane >> 4);
@@ -140,14 +142,14 @@ __device__ __forceinline__ void load_row_scales(const GemmParams& p, int row_bas
   for (int i = 0; i < WM; ++i)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int r = min(row_base + 16 * i + row_lane + v, row_end - 1);
+      const int r = min(row_base + RS * i + row_lane + v, row_end - 1);
       sc[i][v] = !p.row_scale ? 1.0f
                  : FC1       ? p.row_scale[p.row_token[r]]
                              : p.row_scale[r];
     }
 }
 
-template <bool FC1, int WM, int WN>
+template <bool FC1, int WM, int WN, int RS = 16>
 __device__ __forceinline__ void epilogue_sc(const GemmParams& p, const v4f (&acc)[WM][WN],
                                             const float (&sc)[WM][4], int row_base, int row_end,
                                             int nvalid, int64_t nb0, int jvalid, int lane) {
@@ -164,7 +166,7 @@ __device__ __forceinline__ void epilogue_sc(const GemmParams& p, const v4f (&acc
         if (i >= nvalid) continue;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int r = row_base + 16 * i + row_lane + v;
+          const int r = row_base + RS * i + row_lane + v;
           if (r < row_end) {
             const float g = acc[i][2 * q][v] * sc[i][v];
             const float u = acc[i][2 * q + 1][v] * sc[i][v];
@@ -183,7 +185,7 @@ __device__ __forceinline__ void epilogue_sc(const GemmParams& p, const v4f (&acc
         if (i >= nvalid) continue;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int r = row_base + 16 * i + row_lane + v;
+          const int r = row_base + RS * i + row_lane + v;
           if (r < row_end)
             __builtin_nontemporal_store(acc[i][j][v] * sc[i][v], &p.out[(int64_t)r * p.out_stride + c]);
         }
@@ -195,13 +197,13 @@ __device__ __forceinline__ void epilogue_sc(const GemmParams& p, const v4f (&acc
 // Row scales loaded once before any store (the output may alias the scale
 // arrays as far as the compiler knows, so loads placed between stores would
 // each wait for the store before them).
-template <bool FC1, int WM, int WN>
+template <bool FC1, int WM, int WN, int RS = 16>
 __device__ __forceinline__ void epilogue(const GemmParams& p, const v4f (&acc)[WM][WN],
                                          int row_base, int row_end, int nvalid, int64_t nb0,
                                          int jvalid, int lane) {
   float sc[WM][4];
-  load_row_scales<FC1, WM>(p, row_base, row_end, lane, sc);
-  epilogue_sc<FC1, WM, WN>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  load_row_scales<FC1, WM, RS>(p, row_base, row_end, lane, sc);
+  epilogue_sc<FC1, WM, WN, RS>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
 // FC1 epilogue for MX activation formats that quantises the FC2 input in
@@ -212,7 +214,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const v4f (&acc)[W
 // row group.  The h values, the exponent rule and the encoders are the ones
 // the separate FC2 quantiser uses, so the codes are the same bits.  Row
 // scales are 1 for these formats (the caller passes none).
-template <bool E2M1, int WM, int WN>
+template <bool E2M1, int WM, int WN, int RS = 16>
 __device__ __forceinline__ void epilogue_fc1_mx(const GemmParams& p, const v4f (&acc)[WM][WN],
                                                 int row_base, int row_end, int nvalid,
                                                 int64_t nb0, int jvalid, int lane) {
@@ -228,7 +230,7 @@ __device__ __forceinline__ void epilogue_fc1_mx(const GemmParams& p, const v4f (
       if (i >= nvalid) continue;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int r = row_base + 16 * i + row_lane + v;
+        const int r = row_base + RS * i + row_lane + v;
         const float x0 = silu(acc[i][4 * m][v]) * acc[i][4 * m + 1][v];
         const float x1 = silu(acc[i][4 * m + 2][v]) * acc[i][4 * m + 3][v];
         float amax = fmaxf(fabsf(x0), fabsf(x1));
@@ -262,7 +264,7 @@ __device__ __forceinline__ void epilogue_fc1_mx(const GemmParams& p, const v4f (
 // element (no row scale), so GEMM1 writes those bits (q_out, q_stride bytes
 // per row) in place of h: the same h value and rounding as the separate
 // conversion, without the float32 round trip.
-template <int WM, int WN>
+template <int WM, int WN, int RS = 16>
 __device__ __forceinline__ void epilogue_fc1_bf16(const GemmParams& p, const v4f (&acc)[WM][WN],
                                                   int row_base, int row_end, int nvalid,
                                                   int64_t nb0, int jvalid, int lane) {
@@ -277,7 +279,7 @@ __device__ __forceinline__ void epilogue_fc1_bf16(const GemmParams& p, const v4f
       if (i >= nvalid) continue;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int r = row_base + 16 * i + row_lane + v;
+        const int r = row_base + RS * i + row_lane + v;
         if (r < row_end) {
           const float h = silu(acc[i][2 * q][v]) * acc[i][2 * q + 1][v];
           reinterpret_cast<uint16_t*>(p.q_out + (int64_t)r * p.q_stride)[c] = (uint16_t)bf16_bits(h);
@@ -290,23 +292,23 @@ __device__ __forceinline__ void epilogue_fc1_bf16(const GemmParams& p, const v4f
 // End of a GEMM block: the fused FC1 + FC2-input epilogue when the caller
 // asks for it (q_out set) and the format and tile allow it, else the plain
 // epilogue.
-template <int V, bool FC1, int WM, int WN>
+template <int V, bool FC1, int WM, int WN, int RS = 16>
 __device__ __forceinline__ void finish_tile(const GemmParams& p, const v4f (&acc)[WM][WN],
                                             int row_base, int row_end, int nvalid, int64_t nb0,
                                             int jvalid, int lane) {
   if constexpr (FC1 && a_blockscaled(V) && WN % 4 == 0) {
     if (p.q_out) {
-      epilogue_fc1_mx<a_fp4(V), WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+      epilogue_fc1_mx<a_fp4(V), WM, WN, RS>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
       return;
     }
   }
   if constexpr (FC1 && V == kMxfp4Bf16) {
     if (p.q_out) {
-      epilogue_fc1_bf16<WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+      epilogue_fc1_bf16<WM, WN, RS>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
       return;
     }
   }
-  epilogue<FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  epilogue<FC1, WM, WN, RS>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
 hipError_t launch_gemm_direct(int variant, bool fc1, int cfg, const GemmParams& p,

@@ -523,7 +523,8 @@ __global__ __launch_bounds__(kWave * NW, MINB) void k_gemm_ab(GemmParams p) {
 
 // ----------------------------------------------------------------------------
 // Direct-to-LDS grouped GEMM for MXFP4 weights, 160 x 512 block tiles (WM = 5).
-// 8 waves (2 x 4), each 80 rows x 128 device columns (5 x 8 MFMA tiles), so
+// 8 waves (2 x 4), each 80 rows (every second 16-row group of the tile) x
+// 128 device columns (5 x 8 MFMA tiles), so
 // one K step reads 18 KB of operands from LDS per 40 MFMAs per wave (40%
 // less LDS traffic per MFMA than 64 x 64 wave tiles).  160-row tiles
 // let one tile hold an expert of up to 160 rows: a tile costs about the same
@@ -614,9 +615,16 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   constexpr bool PIPE = MXA && !A4 && !FC1;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = lane_id();
   const int wm = wave / kWavesN, wn = wave % kWavesN;
+  // Wave row wm owns the tile's 16-row groups 2i + wm (i < WM), so a partly
+  // filled tile splits its groups evenly between the two waves of a SIMD
+  // (an expert of 128 rows in a 160-row tile: 4 + 4 subtiles, not 5 + 3)
+  constexpr int RS = 32;                   // rows between a wave's subtiles
+  constexpr int kSub = 2 * NF * 1024;      // LDS bytes between a wave's A subtiles
+  constexpr int kSaSub = 2 * 16 * 16;      // the same for the MXFP8 A scales
   const int row_end = tile.row0 + tile.nrows;
-  const int row_base = tile.row0 + 16 * WM * wm;
-  const int nvalid = __builtin_amdgcn_readfirstlane(max(0, min(WM, (row_end - row_base + 15) / 16)));
+  const int row_base = tile.row0 + 16 * wm;
+  const int ngroups = (tile.nrows + 15) / 16;
+  const int nvalid = __builtin_amdgcn_readfirstlane(max(0, min(WM, (ngroups - wm + 1) / 2)));
   const int K = p.K;
   const int KS = K / kKStep, KS4 = (KS + 3) / 4;
   const int64_t e = tile.expert;
@@ -699,7 +707,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   // latency (two dependent loads through row_token for GEMM1) is not paid
   // between the last MFMA and the first output store
   float sc[WM][4];
-  if constexpr (!MXA) load_row_scales<FC1, WM>(p, row_base, row_end, lane, sc);
+  if constexpr (!MXA) load_row_scales<FC1, WM, RS>(p, row_base, row_end, lane, sc);
   uint32_t sx[WN];
   uint4 bq[WN];          // weight fragments (the E2M1 operand is built at each MFMA)
   uint4 alo[2], ahi[2];  // A fragment halves, two subtiles in flight
@@ -711,21 +719,21 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
     return lds + L::kBOff + bst * kBBuf + (wn * WN) * 1024 + lane * 16;
   };
   auto a_at = [&](int ast) __attribute__((always_inline)) {
-    return lds + L::kAOff + ast * L::kABuf + (wm * WM) * (NF * 1024) + lane * 16;
+    return lds + L::kAOff + ast * L::kABuf + wm * (NF * 1024) + lane * 16;
   };
   auto sx_at = [&](int ksx) __attribute__((always_inline)) {
     return lds + L::kSOff + ((ksx >> 2) & 1) * kSxSlot + (wn * WN) * 256 + lane * 4;
   };
-  // MXFP8: A scale dword of subtile i is at + 256 i (row lane%16, k-block lane/16)
+  // MXFP8: A scale dword of subtile i is at + kSaSub i (row lane%16, k-block lane/16)
   auto sa_at = [&](int ksx) __attribute__((always_inline)) {
-    return lds + L::kAsOff + ((ksx >> 2) & 1) * L::kAsSlot + (16 * WM * wm + (lane & 15)) * 16 +
+    return lds + L::kAsOff + ((ksx >> 2) & 1) * L::kAsSlot + (16 * wm + (lane & 15)) * 16 +
            4 * (lane >> 4);
   };
   auto read_a = [&](const uint8_t* as, const uint8_t* sa, int i, int buf)
                     __attribute__((always_inline)) {
-    alo[buf] = *reinterpret_cast<const uint4*>(as + i * 2048);
-    ahi[buf] = *reinterpret_cast<const uint4*>(as + i * 2048 + 1024);
-    if constexpr (MXA) axr[buf] = *reinterpret_cast<const int*>(sa + i * 256);
+    alo[buf] = *reinterpret_cast<const uint4*>(as + i * kSub);
+    ahi[buf] = *reinterpret_cast<const uint4*>(as + i * kSub + 1024);
+    if constexpr (MXA) axr[buf] = *reinterpret_cast<const int*>(sa + i * kSaSub);
   };
 
   // loads per step after the A loads (which come first, 2 or 4 per wave):
@@ -852,15 +860,15 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
 #pragma unroll
         for (int i = 0; i < WM; ++i) {
           if (cols && i < nvalid) {
-            const uint4 lo = *reinterpret_cast<const uint4*>(as + i * (NF * 1024));
+            const uint4 lo = *reinterpret_cast<const uint4*>(as + i * kSub);
             v8i aop;
             if constexpr (A4) {
               aop = fp4_operand(lo);
             } else {
-              const uint4 hi = *reinterpret_cast<const uint4*>(as + i * 2048 + 1024);
+              const uint4 hi = *reinterpret_cast<const uint4*>(as + i * kSub + 1024);
               aop = as_v8i(lo, hi);
             }
-            const int ax = MXA ? *reinterpret_cast<const int*>(sa + i * 256) : 127;
+            const int ax = MXA ? *reinterpret_cast<const int*>(sa + i * kSaSub) : 127;
 #pragma unroll
             for (int j = 0; j < WN; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -913,9 +921,9 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   if (ks + 2 < KS) step(std::integral_constant<int, 2>{}, ks + 2, bstage);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if constexpr (!MXA)
-    epilogue_sc<FC1, WM, WN>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
+    epilogue_sc<FC1, WM, WN, RS>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
   else
-    finish_tile<V, FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+    finish_tile<V, FC1, WM, WN, RS>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
 template <int V, bool FC1, int WM>
