@@ -185,11 +185,23 @@ def compare_all(g, r, wl, exact_rows=True):
     # FC2 input: h differs from the oracle's by float32 rounding, so a few
     # codes (and, rarely, a block exponent at a power-of-two boundary) differ
     if wl.afmt == "fp8":
-        same = np.mean(g["fc2_codes"] == r["fc2_codes"])
+        # Round-to-nearest onto the monotonic E4M3 grid of an h (and a row
+        # scale) that differ from the oracle's by float32 rounding can only
+        # move a code to a neighbouring grid value: every differing code must
+        # be one magnitude step from the oracle's with the same sign, or one
+        # of the two be a zero (a value near zero may also change sign).  A
+        # flipped code is a whole E4M3 step (up to 1/8 of the value), so an
+        # L2 bound on the dequantised input would only count the flips; the
+        # pages' tolerance applies to y2 and the bf16 output below.
+        gc, rc = g["fc2_codes"], r["fc2_codes"]
+        same = np.mean(gc == rc)
         assert same > 0.97, same
-        dq = F.e4m3_decode(g["fc2_codes"]) * g["fc2_scales"][:, None]
-        dr = F.e4m3_decode(r["fc2_codes"]) * r["fc2_scales"][:, None]
-        assert rel_l2(dq, dr) <= 1e-3
+        d = gc != rc
+        gm, rm = (gc[d] & 0x7F).astype(np.int32), (rc[d] & 0x7F).astype(np.int32)
+        same_sign = (gc[d] >> 7) == (rc[d] >> 7)
+        near_zero = np.minimum(gm, rm) == 0
+        ok = (np.abs(gm - rm) == 1) & (same_sign | near_zero) | ((gm == 0) & (rm == 0))
+        assert np.all(ok), np.count_nonzero(~ok)
     if wl.afmt in ("mxfp8", "mxfp4"):
         same = np.mean(g["fc2_codes"] == r["fc2_codes"])
         assert same > 0.97, same
