@@ -182,27 +182,20 @@ def compare_all(g, r, wl, exact_rows=True):
         assert np.array_equal(g["token_block_scales"], r["token_block_scales"]), "token E8M0 differ"
     if g["h"] is not None:
         assert rel_l2(g["h"], r["h"]) <= 1e-4, rel_l2(g["h"], r["h"])
-    # FC2 input: h differs from the oracle's by float32 rounding, so a few
-    # codes (and, rarely, a block exponent at a power-of-two boundary) differ
     if wl.afmt == "fp8":
-        # Round-to-nearest onto the monotonic E4M3 grid of an h (and a row
-        # scale) that differ from the oracle's by float32 rounding can only
-        # move a code to a neighbouring grid value: every differing code must
-        # be one magnitude step from the oracle's with the same sign, or one
-        # of the two be a zero (a value near zero may also change sign).  A
-        # flipped code is a whole E4M3 step (up to 1/8 of the value), so an
-        # L2 bound on the dequantised input would only count the flips; the
-        # pages' tolerance applies to y2 and the bf16 output below.
-        gc, rc = g["fc2_codes"], r["fc2_codes"]
-        same = np.mean(gc == rc)
+        # The FC2 codes and row scales are the oracle's per-row E4M3
+        # quantiser applied to the GPU's own h, bit for bit (h itself is
+        # checked against the oracle's above: it differs by float32
+        # accumulation rounding, so against the oracle's codes a few differ)
+        qc, qs = Q.e4m3_rows(g["h"])
+        assert np.array_equal(g["fc2_codes"], qc), np.count_nonzero(g["fc2_codes"] != qc)
+        assert np.array_equal(g["fc2_scales"].view(np.uint32), qs.view(np.uint32))
+        same = np.mean(g["fc2_codes"] == r["fc2_codes"])
         assert same > 0.97, same
-        d = gc != rc
-        gm, rm = (gc[d] & 0x7F).astype(np.int32), (rc[d] & 0x7F).astype(np.int32)
-        same_sign = (gc[d] >> 7) == (rc[d] >> 7)
-        near_zero = np.minimum(gm, rm) == 0
-        ok = (np.abs(gm - rm) == 1) & (same_sign | near_zero) | ((gm == 0) & (rm == 0))
-        assert np.all(ok), np.count_nonzero(~ok)
     if wl.afmt in ("mxfp8", "mxfp4"):
+        # quantised inside GEMM1's epilogue from an h that is never stored:
+        # codes (and, rarely, a block exponent at a power-of-two boundary)
+        # differ from the oracle's where h rounds differently
         same = np.mean(g["fc2_codes"] == r["fc2_codes"])
         assert same > 0.97, same
         assert np.mean(g["fc2_block_scales"] == r["fc2_block_scales"]) > 0.99
