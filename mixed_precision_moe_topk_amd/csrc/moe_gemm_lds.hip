@@ -609,10 +609,11 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   constexpr int WN = kWN;
   using L = Map<WM, MXA, A4>;
   constexpr int NF = L::kNF;
-  // MXFP8 FC2 inputs: the step order pipelined across the barrier (15 %
-  // faster on the 4096-token DeepSeek-V3 GEMM2; 2-4 % slower than the orders
-  // below on GEMM1 and with per-token E4M3 activations, same-box A/B)
-  constexpr bool PIPE = MXA && !A4 && !FC1;
+  // GEMM2 with E4M3 or MXFP8 inputs: the step order pipelined across the
+  // barrier (same-box A/B against the orders below: MXFP8 4096-token GEMM2
+  // 13 % faster, E4M3 3 % / 5 % on the 4096 / 16384-token DeepSeek GEMM2;
+  // on GEMM1 it was 2-4 % slower)
+  constexpr bool PIPE = !A4 && !FC1;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = lane_id();
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   // Wave row wm owns the tile's 16-row groups 2i + wm (i < WM), so a partly
@@ -760,7 +761,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
       }
     };
     if constexpr (PIPE) {
-      // MXFP8 FC2 inputs, software-pipelined across the barrier:
+      // GEMM2 (E4M3 / MXFP8 inputs), software-pipelined across the barrier:
       // the step enters with its weight fragments, scale words and the A
       // fragment of subtile 0 already in registers; subtile i + 1 is read
       // while the MFMAs of subtile i run; the barrier that publishes the next
@@ -849,7 +850,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
-        // per-token E4M3 and E2M1 (W4A4) activations: the compiler's own
+        // per-token E4M3 GEMM1 and E2M1 (W4A4) activations: the compiler's own
         // order (all of the step's fragments read before the first MFMA)
         // measured 2-3 % faster than the order above
 #pragma unroll
