@@ -1,23 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of the fused mixed-precision MoE layer on one MI355X.
 
-    python bench.py [--workload dsv3_decode_mxfp4_bf16] [--steps K] [--warmup W]
+    python bench.py [--workload dsv4pro_prefill_mxfp4_fp8] [--steps K] [--warmup W]
 
 One step = one pass of the whole layer (routing, token quantisation, GEMM1 +
 SwiGLU, FC2 input, GEMM2, finalize) over one batch of synthetic tokens with
 inputs and packed weights already resident in HBM.  Prints ONE JSON line.
 
-The default workload is the DeepSeek-V3-shaped decode batch (64 tokens, 256
-experts, top-8, hidden 7168, intermediate 2048, MXFP4 weights x BF16
-activations), which is bound by HBM bandwidth: the roofline entry reports the
-GEMM1 kernel's achieved bytes (packed W1 codes + E8M0 scales of every expert
-that receives a token) per launch over its average launch duration, measured
-with HIP events recorded by the library on the kernel's stream.  Prefill
-workloads report GEMM1 FLOP/s against the FP8 (or BF16) MFMA peak instead.
+The default workload is the largest one, the DeepSeek-V4-Pro-shaped prefill
+batch (16384 tokens, 384 experts, top-6, hidden 7168, intermediate 3072,
+MXFP4 weights x per-token E4M3 activations, router logits with a per-expert
+bias for skewed loads), which is bound by the matrix cores: the roofline
+entry reports the GEMM1 kernel's algorithmic FLOP/s (2 * rows * 2I * H per
+launch over its average launch duration, measured with HIP events the
+library records on the kernel's stream) against the FP8 MFMA peak, and
+`layer` the whole layer's GEMM FLOP/s against the same peak.  The
+HBM-bound workloads (decode, INT4) report GEMM1's active-expert weight bytes
+per second against the HBM peak instead.
 
-cpu_baseline: the CPU oracle (float64 NumPy), timed on this host on a bounded
-sample of tokens of the same workload, with expert weights drawn by the host
-generator and quantised before the timed region.
+cpu_baseline: the CPU oracle (float64 NumPy) timed on this host.  Its cost
+is dominated by the expert passes (weight decode plus the rows' GEMMs), so
+it is timed on all tokens with the expert passes of a random sample of whole
+active experts, and once with no expert pass (routing, token quantisation,
+finalize); the layer time is the latter plus the sampled passes scaled by
+active / sampled experts.  Weights are quantised before the timed region.
 """
 from __future__ import annotations
 
@@ -38,10 +44,12 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "mxfp8": 5000.0, "mxfp4": 10100.0, "bf16": 2500.0}
 COPY_CALIB_BYTES = 256 << 20
 METRIC = "fused-MoE tokens/s + % MFMA peak (prefill) / % HBM GB/s (decode), 1 GPU"
-ORACLE_SAMPLE_TOKENS = {"tiny_mxfp4_fp8": 16, "dsv3_decode_mxfp4_bf16": 12,
-                        "dsv3_prefill_mxfp4_fp8": 12, "dsv4pro_prefill_mxfp4_fp8": 24,
-                        "dsv3_int4_fp8": 9, "dsv3_prefill_mxfp4_mxfp8": 12,
-                        "dsv3_prefill_mxfp4_mxfp4": 12}
+# active experts whose whole expert pass the CPU baseline times
+ORACLE_SAMPLE_EXPERTS = {"tiny_mxfp4_fp8": 8, "dsv3_decode_mxfp4_bf16": 16,
+                         "dsv3_prefill_mxfp4_fp8": 8, "dsv4pro_prefill_mxfp4_fp8": 6,
+                         "dsv3_int4_fp8": 10, "dsv3_prefill_mxfp4_mxfp8": 8,
+                         "dsv3_prefill_mxfp4_mxfp4": 8}
+DEFAULT_WORKLOAD = "dsv4pro_prefill_mxfp4_fp8"
 CSRC = "mixed_precision_moe_topk_amd/csrc/"
 
 
@@ -76,7 +84,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dsv3_decode_mxfp4_bf16", choices=sorted(MI.WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(MI.WORKLOADS))
     ap.add_argument("--weights", default="device", choices=["device", "host"],
                     help="draw float32 masters on the device (torch Philox, fast) or with the "
                          "host generator shared with the oracle (slow for 256+ experts)")
@@ -106,24 +114,61 @@ def device_weights(d, wl, torch, chunk=8):
     return weights, scales
 
 
+def cpu_model():
+    """The host CPU's model name (first processor entry of /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl):
+    """Oracle layer time on this host, estimated from timed parts of the
+    oracle on the full workload (see the module docstring)."""
     import oracle as O
 
-    s = min(ORACLE_SAMPLE_TOKENS.get(wl.key, 4), wl.tokens)
-    hb = MI.hidden_bf16(wl.seed, wl.tokens, wl.hidden)[:s]
-    lg = MI.router_logits(wl.seed, wl.tokens, wl.experts, wl.bias_sigma)[:s]
+    hb = MI.hidden_bf16(wl.seed, wl.tokens, wl.hidden)
+    lg = MI.router_logits(wl.seed, wl.tokens, wl.experts, wl.bias_sigma)
     ids, _ = O.route(lg, wl.top_k)
-    need = sorted(set(ids.reshape(-1).tolist()))
+    counts = np.bincount(ids.reshape(-1), minlength=wl.experts)
+    active = np.flatnonzero(counts)
+    by_rows = active[np.argsort(counts[active], kind="stable")]
+    m = min(ORACLE_SAMPLE_EXPERTS.get(wl.key, 8), len(active))
+    # systematic sample over the experts sorted by rows, plus the hottest one
+    pick = ((np.arange(max(m - 1, 1)) + 0.5) * len(by_rows) / max(m - 1, 1)).astype(int)
+    sample = sorted(set(by_rows[pick].tolist()) | {int(by_rows[-1])})
     cache = {}
-    for e, w1, w2 in MI.expert_weights_many(wl.seed, need, wl.hidden, wl.inter):
+    for e, w1, w2 in MI.expert_weights_many(wl.seed, sample, wl.hidden, wl.inter):
         cache[e] = O.quantize_expert(w1, w2, wl.wfmt)  # quantised before the timed region
     t0 = time.perf_counter()
-    O.forward(hb, lg, wl.top_k, lambda e: cache[e], wl.wfmt, wl.afmt)
-    dt = time.perf_counter() - t0
+    O.forward(hb, lg, wl.top_k, lambda e: cache[e], wl.wfmt, wl.afmt, only_experts=set())
+    t1 = time.perf_counter()
+    O.forward(hb, lg, wl.top_k, lambda e: cache[e], wl.wfmt, wl.afmt, only_experts=set(sample))
+    t2 = time.perf_counter()
+    ex = cache[sample[0]]
+    O.layer.decode_weight(ex.w1q, ex.w1s, wl.wfmt)
+    O.layer.decode_weight(ex.w2q, ex.w2s, wl.wfmt)
+    t3 = time.perf_counter()
+    t_tok = t1 - t0                      # routing, token quantisation, finalize
+    t_pass = max(t2 - t1 - t_tok, 0.0)   # the sampled expert passes
+    t_dec = t3 - t2                      # decoding one expert's weights
+    rows_s = int(counts[sample].sum())
+    per_row = max(t_pass - len(sample) * t_dec, 0.0) / max(rows_s, 1)
+    rows = wl.tokens * wl.top_k
+    est = t_tok + len(active) * t_dec + rows * per_row
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    return {"value": round(s / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {s} tokens of the workload ({len(need)} experts), float64 oracle "
-                      f"routing->output, {dt:.2f} s; weights quantised beforehand"}
+    return {"value": round(wl.tokens / est, 2), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"float64 oracle on all {wl.tokens} tokens: routing + token quant + "
+                      f"finalize {t_tok:.2f} s; expert passes of {len(sample)} of the "
+                      f"{len(active)} active experts (the hottest plus a systematic sample by "
+                      f"rows; {rows_s} of {rows} rows) {t_pass:.2f} s; one expert's weight "
+                      f"decode {t_dec:.3f} s; layer estimate {est:.1f} s = token steps + "
+                      f"{len(active)} x decode + {rows} rows x {per_row * 1e3:.3f} ms/row; "
+                      f"weights quantised beforehand"}
 
 
 def main():
@@ -249,6 +294,8 @@ def main():
         "layer": {"weight_GBps": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),
                   "hbm_frac": round(layer_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                   "gemm_TFLOPs": round(layer_flops / (ms_per_step / 1e3) / 1e12, 1),
+                  "mfma_frac": round(layer_flops / (ms_per_step / 1e3) / 1e12
+                                     / MFMA_PEAK_TFLOPS[wl.afmt], 4),
                   "stage_ms": {k: round(v, 4) for k, v in stage_avg.items()}},
     }
     if tuning is not None:

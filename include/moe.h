@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 typedef enum {
   MOE_OK = 0,
@@ -96,8 +96,8 @@ typedef struct {
  *   tok_codes   uint8  [T, H]   E4M3 token codes (FP8 and MXFP8 activations);
  *                      [T, H/2] E2M1 codes, element 2i in the low nibble (MXFP4)
  *   tok_scales  float  [T]      token scales (FP8 activations; 1.0 for MX formats)
- *   h           float  [T*k, I] SwiGLU output per expanded row (not written
- *                               when fc2_fused)
+ *   h           float  [T*k, I] SwiGLU output per expanded row (an empty
+ *                               region, never written, when fc2_fused)
  *   fc2_codes   uint8  [T*k, I] E4M3 (FP8, MXFP8), [T*k, I/2] E2M1 (MXFP4) or
  *                               bf16 bits ([T*k, I] uint16)
  *   fc2_scales  float  [T*k]    per-row FC2 input scale (FP8; not written for
@@ -124,19 +124,31 @@ typedef struct {
   int32_t fc2_fused;
 } moe_ws_layout;
 
+/* Version of this ABI (MOE_ABI_VERSION of the header the library was built
+ * with); a binding compares it with its own before any other call. */
 int32_t moe_abi_version(void);
 
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of the last failed call on this thread ("" if none).  Errors are
+ * reported, never raised or printed: flashinfer PR #3614 ("fix: make the
+ * cutlass MoE gemm profiler MXFP8-aware ...", Description) traces an
+ * autotune crash to an assertion deep inside a kernel launcher; here a bad
+ * argument is a status code and a message before any launch. */
 const char* moe_last_error(void);
 
 /* Bytes of the packed weights and of the scales for all experts (pure host
- * arithmetic).  Per expert: codes (2*I*H + H*I)/2 bytes; scales
+ * arithmetic; flashinfer PR #3738, Implementation Notes: one folded
+ * weight-scale layout serves every K tile, so the sizes depend on the shape
+ * and formats only, never on the tile configuration).  Per expert: codes (2*I*H + H*I)/2 bytes; scales
  * 2*I*ceil(H/512)*16 + H*ceil(I/512)*16 bytes (MXFP4) or
  * 4*(2*I*H + H*I)/128 bytes (INT4). */
 moe_status moe_weights_query(const moe_dims* dims, size_t* weight_bytes, size_t* scale_bytes);
 
 /* Quantises float32 master weights of experts [expert_begin, expert_begin +
- * expert_count) into the device layout.
+ * expert_count) into the device layout (flashinfer PR #3738, Description:
+ * MXFP4 weights with one E8M0 scale per 32 elements along K, INT4 weights
+ * with group scales; Implementation Notes: weight preprocessing into a
+ * folded weight-scale layout independent of the GEMM's K tile — here the
+ * matrix-core operand order, with one 16-byte scale group per four K steps).
  *   w1: device float [expert_count, 2*inter, hidden]
  *   w2: device float [expert_count, hidden, inter]
  *   weights, scales: device buffers of moe_weights_query's sizes (all experts);
@@ -150,7 +162,9 @@ moe_status moe_prepare_weights(const moe_dims* dims, const float* w1, const floa
                                int32_t expert_begin, int32_t expert_count, void* weights,
                                void* scales, hipStream_t stream);
 
-/* Inverse of the device layout, for checking codes bit for bit: writes the
+/* Inverse of the device layout (moe_prepare_weights; flashinfer PR #3738,
+ * Implementation Notes, folded weight-scale layout), for checking codes bit
+ * for bit: writes the
  * canonical row-major codes and scales of experts [expert_begin,
  * expert_begin + expert_count) into device buffers
  *   w1q uint8 [n, 2*inter, hidden/2]   (element 2i in the low nibble;
@@ -162,17 +176,31 @@ moe_status moe_unpack_weights(const moe_dims* dims, const void* weights, const v
                               int32_t expert_begin, int32_t expert_count, void* w1q, void* w1s,
                               void* w2q, void* w2s, hipStream_t stream);
 
-/* Workspace bytes moe_run_ws needs for num_tokens tokens and top_k. */
+/* Workspace bytes moe_run_ws needs for num_tokens tokens and top_k (the
+ * caller-owned workspace and its size query that flashinfer's fused MoE
+ * keeps: PR #4411 page, "revert(moe): revert #3738 ...", Conflict
+ * resolution, cutlass_fused_moe_workspace_size / workspace_buffer).  Errors:
+ * MOE_ERR_INVALID_ARG for bad dims, num_tokens < 0 or > 2^26, top_k outside
+ * [1, min(num_experts, 16)] or a null output pointer. */
 moe_status moe_workspace_query(const moe_dims* dims, int64_t num_tokens, int32_t top_k,
                                size_t* bytes);
 
-/* Offsets of the intermediates inside that workspace. */
+/* Offsets of the intermediates inside that workspace (same page and section
+ * as moe_workspace_query; the tests read the routing maps, token codes and
+ * GEMM outputs at these offsets).  Errors as moe_workspace_query. */
 moe_status moe_workspace_layout(const moe_dims* dims, int64_t num_tokens, int32_t top_k,
                                 moe_ws_layout* layout);
 
-/* Runs the layer with a caller-owned workspace.
+/* Runs the layer with a caller-owned workspace (flashinfer PR #3738,
+ * Description: routing, expansion with runtime per-token FP8 quantisation,
+ * grouped GEMM1 over MXFP4 / INT4 weights with the activation, grouped GEMM2
+ * and the weighted top-k reduction; the caller-owned workspace as kept by
+ * the PR #4411 page, Conflict resolution).
  *   hidden:        device bf16 bits [num_tokens, hidden]
- *   router_logits: device float [num_tokens, num_experts] (finite values)
+ *   router_logits: device float [num_tokens, num_experts]; a NaN logit ranks
+ *                  as -inf, so every selected id is a valid expert index; a
+ *                  token whose largest selected logit is infinite (or whose
+ *                  logits are all NaN) gets NaN weights and a NaN output row
  *   weights, scales: prepared by moe_prepare_weights for all experts
  *   out:           device bf16 bits [num_tokens, hidden], fully overwritten
  *   workspace:     device buffer of at least moe_workspace_query bytes
@@ -185,18 +213,42 @@ moe_status moe_run_ws(const moe_dims* dims, const void* hidden, int64_t num_toke
                       int32_t top_k, void* out, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
-/* Same as moe_run_ws, with a workspace the library keeps per (device,
- * stream) and grows stream-ordered (hipMallocAsync) when a call needs more.
- * Calls on different streams use different workspaces. */
+/* Same as moe_run_ws (flashinfer PR #3738, Description), with a workspace the
+ * library keeps per (device, stream) and grows stream-ordered
+ * (hipMallocAsync) when a call needs more: the library-managed workspace the
+ * fused MoE uses when the caller passes none (PR #4411 page, Conflict
+ * resolution).  Calls on different streams use different workspaces; an
+ * arena lives until moe_release_arenas or the end of the process.  Errors
+ * as moe_run_ws, plus MOE_ERR_HIP when the arena cannot grow. */
 moe_status moe_run(const moe_dims* dims, const void* hidden, int64_t num_tokens,
                    const float* router_logits, const void* weights, const void* scales,
                    int32_t top_k, void* out, hipStream_t stream);
+
+/* Frees every workspace moe_run holds (all devices and streams).  Waits for
+ * each device that holds one (hipDeviceSynchronize), so no call may be in
+ * flight on another thread.  The next moe_run allocates again.  Errors:
+ * MOE_ERR_HIP if a device call fails (the remaining arenas are still freed). */
+moe_status moe_release_arenas(void);
+
+/* Test hook for the FC2 input of the fused epilogues (flashinfer PR #3738,
+ * Implementation Notes: tactics are checked for correctness against a
+ * reference path).  enable = 1 (the default): GEMM1 writes the FC2 input
+ * itself where the format and tile allow it (MX activation formats, BF16), so
+ * float32 h is never stored.  enable = 0: GEMM1 stores h and the separate FC2
+ * quantiser runs for every format; moe_workspace_layout then reports
+ * fc2_fused = 0 and reserves h.  Both give the same FC2 bytes (the fused
+ * epilogue applies the same quantiser to the same h values), which the
+ * tests check bit for bit.  Process-wide; it changes the workspace size, so
+ * set it only while no call is in flight.  Errors: MOE_ERR_INVALID_ARG unless
+ * enable is 0 or 1. */
+moe_status moe_set_fc2_fused(int32_t enable);
 
 /* The routing step of the run calls alone, same kernels (flashinfer PR #4793,
  * Walkthrough: the fused MoE consumes the router's selected experts and final
  * scales; flashinfer PR #3738, Implementation Notes: the grouped GEMM's
  * per-expert work map is computed on the device before the GEMMs).
- *   router_logits:  device float [num_tokens, num_experts] (finite values)
+ *   router_logits:  device float [num_tokens, num_experts]; NaN ranks as
+ *                   -inf (see moe_run_ws)
  *   ids:            device int32 [num_tokens, top_k] out: the k largest logits
  *                   per token in descending order, equal logits by the smaller
  *                   expert index

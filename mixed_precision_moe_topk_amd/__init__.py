@@ -24,8 +24,9 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_weights_query", "moe_prepare_weights",
            "moe_unpack_weights", "moe_workspace_query", "moe_workspace_layout", "moe_run_ws",
-           "moe_run", "moe_route", "moe_quantize_tokens", "moe_tune_set", "moe_tune_clear", "moe_autotune", "moe_trace_enable",
-           "moe_trace_read")
+           "moe_run", "moe_route", "moe_quantize_tokens", "moe_tune_set", "moe_tune_clear",
+           "moe_autotune", "moe_trace_enable", "moe_trace_read", "moe_release_arenas",
+           "moe_set_fc2_fused")
 STAGES = ("route", "quant", "gemm1", "requant", "gemm2", "finalize")
 
 
@@ -79,6 +80,8 @@ def lib():
             "moe_autotune": [DP, P, I64, P, P, P, I32, I32, ctypes.POINTER(I32),
                              ctypes.POINTER(ctypes.c_float), P],
             "moe_trace_enable": [I32],
+            "moe_release_arenas": [],
+            "moe_set_fc2_fused": [I32],
             "moe_trace_read": [ctypes.POINTER(ctypes.c_float), I32, ctypes.POINTER(I32)],
         }
         for name, args in sig.items():
@@ -239,3 +242,15 @@ def trace_read():
     calls = ctypes.c_int32()
     _check(lib().moe_trace_read(arr, n, ctypes.byref(calls)))
     return calls.value, {s: float(arr[i]) for i, s in enumerate(STAGES)}
+
+
+def release_arenas():
+    """Frees the workspaces moe_run keeps per device and stream."""
+    _check(lib().moe_release_arenas())
+
+
+def set_fc2_fused(enable: bool):
+    """Test hook: False makes GEMM1 store float32 h and the separate FC2
+    quantiser run for every format (process-wide; changes the workspace
+    layout)."""
+    _check(lib().moe_set_fc2_fused(1 if enable else 0))

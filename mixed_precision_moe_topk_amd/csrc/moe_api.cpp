@@ -15,6 +15,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <map>
 #include <mutex>
@@ -164,6 +165,12 @@ int cfg_for(const moe_dims* d, int64_t T, int32_t k, int force) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// moe_set_fc2_fused: 0 makes GEMM1 store float32 h and the separate FC2
+// quantiser run for every format (the checked reference of the fused
+// epilogues); 1 (the default) lets GEMM1 write the FC2 input itself where
+// the format and tile allow it.
+std::atomic<int> g_fc2_fusion{1};
+
 // Workspace layout; force >= 0 selects the tile configuration.  The regions
 // do not depend on the configuration (the work map has room for 16-row
 // tiles), so tuning never changes the workspace size.
@@ -200,9 +207,15 @@ moe_status layout_of(const moe_dims* d, int64_t T, int32_t k, moe_ws_layout* L, 
   const bool e2m1 = d->afmt == MOE_A_MXFP4;
   const bool e4m3 = d->afmt == MOE_A_FP8_TOKEN || d->afmt == MOE_A_MXFP8;
   const bool mx = d->afmt == MOE_A_MXFP8 || e2m1;
+  // GEMM1 writes the FC2 input itself: MX formats on waves whose tiles hold
+  // whole 32-column blocks of h (4 column blocks), BF16 always (bf16(h) is
+  // element-wise); then h is never stored and takes no workspace
+  const int fused = g_fc2_fusion.load(std::memory_order_relaxed) &&
+                    ((mx && moe::gemm_cfg(cfg, variant_of(d)).wn % 4 == 0) ||
+                     d->afmt == MOE_A_BF16);
   L->tok_codes = take(e4m3 ? T * H : e2m1 ? T * H / 2 : 0);
   L->tok_scales = take(e4m3 || e2m1 ? T * 4 : 0);
-  L->h = take(rows * I * 4);
+  L->h = take(fused ? 0 : rows * I * 4);
   L->fc2_codes = take(e4m3 ? rows * I : e2m1 ? rows * I / 2 : rows * I * 2);
   L->fc2_scales = take(rows * 4);
   L->y2 = take(rows * H * 4);
@@ -212,10 +225,7 @@ moe_status layout_of(const moe_dims* d, int64_t T, int32_t k, moe_ws_layout* L, 
   L->tile_m = tile_m;
   L->gemm_cfg = cfg;
   L->max_tiles = max_tiles;
-  // GEMM1 writes the FC2 input itself: MX formats on waves whose tiles hold
-  // whole 32-column blocks of h (4 column blocks), BF16 always (bf16(h) is
-  // element-wise)
-  L->fc2_fused = (mx && moe::gemm_cfg(cfg, variant_of(d)).wn % 4 == 0) || d->afmt == MOE_A_BF16;
+  L->fc2_fused = fused;
   return MOE_OK;
 }
 
@@ -554,6 +564,13 @@ moe_status run_checked(const moe_dims* dims, const void* hidden, int64_t num_tok
   return ok();
 }
 
+// Library workspaces of moe_run, per (device, stream).
+std::mutex g_arena_mu;
+std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>>& arenas() {
+  static std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> a;
+  return a;
+}
+
 // Host copy of a bf16 device buffer as float.
 moe_status fetch_bf16(const void* dev, size_t n, std::vector<float>* outv) {
   std::vector<uint16_t> bits(n);
@@ -762,16 +779,14 @@ moe_status moe_run(const moe_dims* dims, const void* hidden, int64_t num_tokens,
   moe_ws_layout L;
   MOE_TRY(layout_of(dims, num_tokens, top_k, &L));
   if (num_tokens == 0) return ok();
-  static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> arenas;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
   void* ws = nullptr;
   size_t cap = 0;
   {
-    std::lock_guard<std::mutex> lk(mu);
-    auto& slot = arenas[{dev, stream}];
+    std::lock_guard<std::mutex> lk(g_arena_mu);
+    auto& slot = arenas()[{dev, stream}];
     if (slot.second < L.total) {
       if (slot.first) {
         e = hipFreeAsync(slot.first, stream);
@@ -788,6 +803,34 @@ moe_status moe_run(const moe_dims* dims, const void* hidden, int64_t num_tokens,
   }
   return moe_run_ws(dims, hidden, num_tokens, router_logits, weights, scales, top_k, out, ws,
                     cap, stream);
+}
+
+moe_status moe_release_arenas(void) {
+  std::lock_guard<std::mutex> lk(g_arena_mu);
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  moe_status st = MOE_OK;
+  for (auto& kv : arenas()) {
+    if (!kv.second.first) continue;
+    // the arena's last user may still run on its stream: wait for the device
+    e = hipSetDevice(kv.first.first);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipFree(kv.second.first);
+    if (e != hipSuccess && st == MOE_OK)
+      st = fail(MOE_ERR_HIP, "releasing the workspace of device %d: %s", kv.first.first,
+                hipGetErrorString(e));
+  }
+  arenas().clear();
+  e = hipSetDevice(cur);
+  if (e != hipSuccess && st == MOE_OK) st = fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(e));
+  return st == MOE_OK ? ok() : st;
+}
+
+moe_status moe_set_fc2_fused(int32_t enable) {
+  if (enable != 0 && enable != 1) return fail(MOE_ERR_INVALID_ARG, "enable %d is not 0 or 1", enable);
+  g_fc2_fusion.store(enable, std::memory_order_relaxed);
+  return ok();
 }
 
 }  // extern "C"

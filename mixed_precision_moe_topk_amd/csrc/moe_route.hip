@@ -40,7 +40,10 @@ __device__ __forceinline__ void route_token(const RouteParams& p, const int64_t 
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + i * kWave;
-    v[i] = (e < E) ? row[e] : 0.0f;
+    const float x = (e < E) ? row[e] : 0.0f;
+    // a NaN logit ranks as -inf: every round then has a holder of the
+    // maximum (-inf at worst), so every id is a valid expert index
+    v[i] = x == x ? x : -INFINITY;
     if (e >= E) taken |= 1u << i;
   }
 

@@ -44,8 +44,15 @@ from . import quant as Q
 
 
 def route(logits: np.ndarray, top_k: int):
-    """logits float32 [T, E] -> (ids int32 [T, k], weights float32 [T, k])."""
+    """logits float32 [T, E] -> (ids int32 [T, k], weights float32 [T, k]).
+
+    The pages say nothing of non-finite logits.  Reading taken here (and by
+    the GPU router): a NaN logit ranks as -inf, so every id stays a valid
+    expert index; infinite logits rank as their values.  When the largest
+    selected logit is infinite the softmax is undefined and the weights come
+    out NaN (exp(inf - inf))."""
     logits = np.asarray(logits, dtype=np.float32)
+    logits = np.where(np.isnan(logits), np.float32(-np.inf), logits)
     t, e = logits.shape
     assert 1 <= top_k <= e
     idx = np.broadcast_to(np.arange(e), (t, e))
@@ -54,8 +61,9 @@ def route(logits: np.ndarray, top_k: int):
     order = np.lexsort((idx, -logits.astype(np.float64)), axis=-1)
     ids = order[:, :top_k].astype(np.int32)
     sel = np.take_along_axis(logits, ids.astype(np.int64), axis=1).astype(np.float64)
-    p = np.exp(sel - sel[:, :1])
-    w = (p / p.sum(axis=1, keepdims=True)).astype(np.float32)
+    with np.errstate(invalid="ignore"):  # inf - inf: undefined softmax -> NaN weights
+        p = np.exp(sel - sel[:, :1])
+        w = (p / p.sum(axis=1, keepdims=True)).astype(np.float32)
     return ids, w
 
 
@@ -115,10 +123,18 @@ def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
 
 def forward(hidden_bits: np.ndarray, logits: np.ndarray, top_k: int,
             expert_fn: Callable[[int], ExpertWeights], wfmt: str, afmt: str,
-            check_exact: bool = True, keep_y1: bool = False) -> dict:
+            check_exact: bool = True, keep_y1: bool = False,
+            only_experts=None) -> dict:
     """Runs the layer.  hidden_bits: bf16 bits uint16 [T, H]; logits float32
     [T, E]; expert_fn(e) returns the canonical weights of expert e (called
-    once per expert that receives rows).  Returns every intermediate."""
+    once per expert that receives rows).  Returns every intermediate.
+
+    only_experts (a set of expert ids, or None for all): the expert passes
+    (GEMM1, SwiGLU, FC2 input, GEMM2) run for these experts only and the
+    rows of the others keep h = y2 = 0; routing, token quantisation and the
+    finalize always run over all tokens.  Used to time the oracle on a
+    sample of whole experts; the arithmetic of a pass that runs is the
+    same."""
     t, h = hidden_bits.shape
     e_num = logits.shape[1]
     ids, w = route(logits, top_k)
@@ -148,7 +164,7 @@ def forward(hidden_bits: np.ndarray, logits: np.ndarray, top_k: int,
     h_all = y2 = q2 = s2 = sx2 = y1_all = None
     for e in range(e_num):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
-        if r1 == r0:
+        if r1 == r0 or (only_experts is not None and e not in only_experts):
             continue
         wts = expert_fn(e)
         toks = row_tok[r0:r1]
@@ -204,6 +220,8 @@ def forward(hidden_bits: np.ndarray, logits: np.ndarray, top_k: int,
         w2 = decode_weight(wts.w2q, wts.w2s, wfmt)
         acc2 = a2 @ w2.T
         y2[r0:r1] = (acc2 * ss[:, None].astype(np.float64)).astype(np.float32)
+    if y2 is None:  # no expert pass ran (empty batch, or an empty only_experts)
+        y2 = np.zeros((rows, h), dtype=np.float32)
     acc_out = np.zeros((t, h), dtype=np.float32)
     for j in range(top_k if t else 0):
         term = (w[:, j:j + 1] * y2[slot_row[:, j]]).astype(np.float32)

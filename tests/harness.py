@@ -192,10 +192,20 @@ def compare_all(g, r, wl, exact_rows=True):
         assert np.array_equal(g["fc2_scales"].view(np.uint32), qs.view(np.uint32))
         same = np.mean(g["fc2_codes"] == r["fc2_codes"])
         assert same > 0.97, same
+    if g["h"] is not None and wl.afmt in ("mxfp8", "mxfp4", "bf16"):
+        # h stored (the separate FC2 quantiser ran): its bytes are the
+        # oracle's quantiser applied to the GPU's own h, bit for bit
+        if wl.afmt == "bf16":
+            assert np.array_equal(g["fc2_codes"], F.bf16_rne(g["h"])), "FC2 bf16 bits"
+        else:
+            quant = Q.mxfp8_rows if wl.afmt == "mxfp8" else Q.mxfp4_quantize
+            qc, qs = quant(g["h"])
+            assert np.array_equal(g["fc2_codes"], qc), np.count_nonzero(g["fc2_codes"] != qc)
+            assert np.array_equal(g["fc2_block_scales"], qs), "FC2 E8M0 codes"
     if wl.afmt in ("mxfp8", "mxfp4"):
-        # quantised inside GEMM1's epilogue from an h that is never stored:
-        # codes (and, rarely, a block exponent at a power-of-two boundary)
-        # differ from the oracle's where h rounds differently
+        # secondary check against the oracle's own FC2 input (quantised from
+        # the oracle's h): codes (and, rarely, a block exponent at a
+        # power-of-two boundary) differ where h rounds differently
         same = np.mean(g["fc2_codes"] == r["fc2_codes"])
         assert same > 0.97, same
         assert np.mean(g["fc2_block_scales"] == r["fc2_block_scales"]) > 0.99
@@ -204,8 +214,8 @@ def compare_all(g, r, wl, exact_rows=True):
         dr = dec(r["fc2_codes"], r["fc2_block_scales"])
         assert rel_l2(dq, dr) <= 1e-3
     if wl.afmt == "bf16":
-        # FC2 input bf16(h) (written by GEMM1's epilogue): h differs from the
-        # oracle's by float32 rounding, so a few values round to the
+        # secondary check against the oracle's own bf16(h): h differs from
+        # the oracle's by float32 rounding, so a few values round to the
         # neighbouring bf16
         same = np.mean(g["fc2_codes"] == r["fc2_codes"])
         assert same > 0.97, same

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == set(M.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 6
+    assert L.moe_abi_version() == 7
 
 
 def _d(**kw):
@@ -211,3 +211,29 @@ def test_stage_calls_reject_before_launch(L):
     mx = _d(num_experts=8, hidden=256, inter=512, afmt="mxfp8").c()
     assert L.moe_quantize_tokens(ctypes.byref(mx), ok, 4, ok, ok, None, None) == 1  # needs block scales
     assert L.moe_quantize_tokens(ctypes.byref(mx), ok, 4, ok, ok, bad, None) == 1
+
+
+@pytest.mark.parametrize("afmt", ["bf16", "mxfp8", "mxfp4", "fp8"])
+def test_fc2_fusion_switch_changes_the_layout(L, afmt):
+    """moe_set_fc2_fused(0) makes every format store h (reserved in the
+    workspace) and run the separate FC2 quantiser; with fusion (the default)
+    the MX formats and BF16 reserve no h."""
+    d = _d(afmt=afmt)
+    T, k = 300, 8
+    fused = M.workspace_layout(d, T, k)
+    try:
+        M.set_fc2_fused(False)
+        plain = M.workspace_layout(d, T, k)
+    finally:
+        M.set_fc2_fused(True)
+    assert plain.fc2_fused == 0
+    assert plain.fc2_codes - plain.h >= T * k * 2048 * 4
+    if afmt == "fp8":
+        assert fused.fc2_fused == 0 and fused.total == plain.total
+    else:
+        assert fused.fc2_fused == 1 and fused.fc2_codes == fused.h
+        assert plain.total - fused.total >= T * k * 2048 * 4
+    assert M.workspace_layout(d, T, k).total == fused.total
+    with pytest.raises(M.MoeError) as ei:
+        _ = L.moe_set_fc2_fused(2) and M._check(L.moe_set_fc2_fused(2))
+    assert ei.value.status == 1

@@ -1,9 +1,14 @@
 """GPU parity at the full DeepSeek-V3 / V4-Pro sizes, in the launch
 configuration the benchmark times: routing ids, expert row maps and E4M3
 token codes for every token (bit-exact); prepared weight codes for sampled
-experts (bit-exact); SwiGLU output, GEMM2 output and the bf16 layer output
-for a sample of tokens, computed one by one by the oracle (the layer is
-independent per token), within the output contract.
+experts (bit-exact); the per-token E4M3 FC2 codes of every row against the
+oracle's quantiser of the GPU's h (bit-exact); SwiGLU and GEMM2 output of
+chosen rows (every row of the last, partial M-tile and of the second 16-row
+group of the first tile, for the hottest, the coldest and random experts:
+the tile tails and the second wave row), against the oracle's pass of that
+one expert; and the bf16 layer output for random tokens, computed token by
+token by the oracle (the layer is independent per token), within the output
+contract.
 
 Only experts that receive tokens are prepared (the others are never read)."""
 import numpy as np
@@ -19,12 +24,13 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 CASES = ["dsv3_decode_mxfp4_bf16", "dsv3_int4_fp8", "dsv3_prefill_mxfp4_fp8",
          "dsv4pro_prefill_mxfp4_fp8", "dsv3_prefill_mxfp4_mxfp8", "dsv3_prefill_mxfp4_mxfp4"]
 SAMPLE = 3  # tokens checked against the oracle end to end
+CHECK_EXPERTS = 6  # experts whose tile tails are checked row by row
 
 
 class ActiveProblem(Problem):
     """Problem whose device weights cover only the experts with routed rows."""
 
-    def __init__(self, wl, sample_tokens):
+    def __init__(self, wl, sample_tokens, extra_experts=()):
         import torch
 
         import mixed_precision_moe_topk_amd as M
@@ -37,6 +43,7 @@ class ActiveProblem(Problem):
         self.ref_ids = ids
         active = sorted(set(ids.reshape(-1).tolist()))
         want = set(ids[sample_tokens].reshape(-1).tolist()) | {active[0], active[-1]}
+        want |= set(extra_experts)
         self.oracle_w = {}
         wb, sb = M.weights_query(self.dims)
         self.weights = torch.zeros(wb, dtype=torch.uint8, device="cuda")
@@ -61,7 +68,14 @@ def test_fullsize_sampled(name):
     wl = MI.WORKLOADS[name]
     rng = np.random.default_rng(wl.seed)
     sample = np.sort(rng.choice(wl.tokens, size=SAMPLE, replace=False))
-    p = ActiveProblem(wl, sample)
+    # experts whose tile tails are checked: the hottest, the coldest, random
+    logits = MI.router_logits(wl.seed, wl.tokens, wl.experts, wl.bias_sigma)
+    counts = np.bincount(O.route(logits, wl.top_k)[0].reshape(-1), minlength=wl.experts)
+    act = np.flatnonzero(counts)
+    chk = {int(act[np.argmax(counts[act])]), int(act[np.argmin(counts[act])])}
+    chk |= set(rng.choice(act, size=CHECK_EXPERTS, replace=False).tolist())
+    chk = sorted(chk)[:CHECK_EXPERTS + 2]
+    p = ActiveProblem(wl, sample, chk)
     g = p.run_gpu()
     print(f"{name}: tile_m={g['tile_m']} tiles={g['num_tiles']} active={len(p.active)}")
     # routing and row maps for every token
@@ -89,6 +103,54 @@ def test_fullsize_sampled(name):
         assert np.array_equal(q1[0], ow.w1q) and np.array_equal(q2[0], ow.w2q)
         assert np.array_equal(s1[0].view(np.uint8), np.ascontiguousarray(ow.w1s).view(np.uint8))
         assert np.array_equal(s2[0].view(np.uint8), np.ascontiguousarray(ow.w2s).view(np.uint8))
+    # per-token E4M3 FC2 input of every row: the oracle's quantiser of the
+    # GPU's h, bit for bit
+    if wl.afmt == "fp8":
+        qc, qs = O.quant.e4m3_rows(g["h"])
+        assert np.array_equal(g["fc2_codes"], qc)
+        assert np.array_equal(g["fc2_scales"].view(np.uint32), qs.view(np.uint32))
+    # FC2 input written by GEMM1's epilogue (MX formats, BF16): equal, bit
+    # for bit, to the separate quantiser's output on the stored h, which is
+    # the oracle's quantiser applied to that h
+    if wl.afmt in ("mxfp8", "mxfp4", "bf16"):
+        import mixed_precision_moe_topk_amd as M
+
+        assert g["fc2_fused"]
+        M.set_fc2_fused(False)
+        try:
+            gu = p.run_gpu()
+        finally:
+            M.set_fc2_fused(True)
+        if wl.afmt == "bf16":
+            assert np.array_equal(gu["fc2_codes"], F.bf16_rne(gu["h"]))
+        else:
+            quant = O.quant.mxfp8_rows if wl.afmt == "mxfp8" else O.quant.mxfp4_quantize
+            qc, qs = quant(gu["h"])
+            assert np.array_equal(gu["fc2_codes"], qc)
+            assert np.array_equal(gu["fc2_block_scales"], qs)
+            assert np.array_equal(g["fc2_block_scales"], gu["fc2_block_scales"])
+        assert np.array_equal(g["fc2_codes"], gu["fc2_codes"])
+        assert np.array_equal(g["out"], gu["out"])
+        g["h"] = gu["h"]
+        del gu
+    # tile tails of chosen experts: every row of the last (partial) M-tile and
+    # of rows 16-31 of the first tile (the second wave row), against the
+    # oracle's pass of that one expert over those rows' tokens
+    tm = g["tile_m"]
+    for e in chk:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        last = r0 + ((r1 - r0 - 1) // tm) * tm
+        rows_e = sorted(set(range(last, r1)) | set(range(min(r0 + 16, r1), min(r0 + 32, r1))))
+        toks = np.unique(tok[rows_e])
+        sub = O.forward(p.hidden[toks], p.logits[toks], wl.top_k, lambda x: p.oracle_w[x],
+                        wl.wfmt, wl.afmt, only_experts={e})
+        ti, tj = np.nonzero(sub["ids"] == e)
+        grow = g["slot_row"][toks[ti], tj]
+        orow = sub["slot_row"][ti, tj]
+        if g["h"] is not None:
+            assert rel_l2(g["h"][grow], sub["h"][orow]) <= 1e-4, e
+        assert rel_l2(g["y2"][grow], sub["y2"][orow]) <= 2e-3, e
+        print(f"{name}: expert {e} ({r1 - r0} rows, tile_m {tm}): {len(grow)} tail rows checked")
     # sampled tokens end to end
     r = p.run_oracle(tokens=sample)
     rows = g["slot_row"][sample].reshape(-1)

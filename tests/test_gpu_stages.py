@@ -67,6 +67,39 @@ def test_route_matches_oracle(T, E, k, bias, grid, seed):
     assert np.array_equal(tiles, expected_work_map(roff, lay.tile_m))
 
 
+def test_route_nan_logits_rank_as_minus_infinity():
+    """Regression: NaN logits (a whole row, and scattered entries) rank as
+    -inf on the GPU as in the oracle; every id is a valid expert index and
+    the row maps stay a permutation; finite weights match, NaN weights sit
+    where the oracle's do."""
+    import torch
+
+    import mixed_precision_moe_topk_amd as M
+
+    T, E, k = 70, 256, 8
+    logits = MI.router_logits(110, T, E)
+    logits[3, :] = np.nan
+    logits[5, ::3] = np.nan
+    logits[9, 10] = np.nan
+    logits[11, :] = -np.inf
+    d = M.LayerDims(E, 256, 256, "mxfp4", "fp8")
+    ws = torch.full((M.workspace_query(d, T, k),), 0xA5, dtype=torch.uint8, device="cuda")
+    ids, w, off, rt, sr = _route_outputs(torch, T, E, k)
+    M.route(d, torch.from_numpy(logits).cuda(), k, ids, w, off, rt, sr, ws)
+    torch.cuda.synchronize()
+    rid, rw = O.route(logits, k)
+    roff, rrt, _, rsr = O.expand(rid, E)
+    g_ids, g_w = ids.cpu().numpy(), w.cpu().numpy()
+    assert np.array_equal(g_ids, rid)
+    assert g_ids.min() >= 0 and g_ids.max() < E
+    assert np.array_equal(np.isnan(g_w), np.isnan(rw))
+    fin = ~np.isnan(rw)
+    assert np.max(np.abs(g_w[fin] - rw[fin])) <= 1e-6
+    assert np.array_equal(off.cpu().numpy(), roff.astype(np.int32))
+    assert np.array_equal(rt.cpu().numpy(), rrt.astype(np.int32))
+    assert np.array_equal(sr.cpu().numpy(), rsr.astype(np.int32))
+
+
 def test_route_into_workspace_regions():
     """Outputs placed at the workspace offsets moe_run_ws uses give the same
     bits as separate buffers."""

@@ -1,9 +1,13 @@
 """Tile-configuration selection on the GPU: every configuration of every format
 combination matches the oracle (forced through the tuning table, on skewed
 routing), the configurations give identical bits (each K step is accumulated
-in the same order by the same matrix instruction whatever the tile shape; the
-FC2 input that GEMM1 quantises itself for the MX formats equals the separate
-quantiser's), and the autotuner validates, times and stores its choice."""
+in the same order by the same matrix instruction whatever the tile shape),
+and the autotuner validates, times and stores its choice.
+
+The FC2 input that GEMM1 writes itself (MX formats, BF16) is checked bit for
+bit: with the fusion switched off GEMM1 stores h and the separate quantiser
+runs, whose bytes must equal the oracle's quantiser applied to that h
+(compare_all), and the fused run's bytes must equal the separate ones."""
 import numpy as np
 import pytest
 
@@ -35,8 +39,20 @@ def test_every_tile_config_matches_oracle(wf, af):
             rel, mx = compare_all(g, r, wl)
             print(f"{wf}x{af} cfg {c} tile_m={g['tile_m']} tiles={g['num_tiles']} rel-L2={rel:.2e}")
             runs[c] = g
+            if af in ("mxfp8", "mxfp4", "bf16"):
+                M.set_fc2_fused(False)
+                try:
+                    gu = p.run_gpu()
+                finally:
+                    M.set_fc2_fused(True)
+                assert not gu["fc2_fused"] and gu["h"] is not None
+                compare_all(gu, r, wl)  # separate quantiser == oracle's quantiser of this h
+                fkeys = ["fc2_codes", "y2", "out"] + (["fc2_block_scales"] if af != "bf16" else [])
+                for key in fkeys:
+                    assert np.array_equal(g[key].view(np.uint8), gu[key].view(np.uint8)), (c, key)
     finally:
         M.tune_clear()
+        M.set_fc2_fused(True)
     keys = ["fc2_codes", "y2", "out"]
     if af in ("mxfp8", "mxfp4", "bf16"):
         # every configuration writes the FC2 input from GEMM1 (no h)

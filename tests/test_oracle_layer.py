@@ -322,3 +322,93 @@ def test_per_token_independence_and_empty():
     assert np.array_equal(part["out"], full["out"][sub])
     empty = O.forward(hb[:0], lg[:0], 2, lambda e: ex[e], "mxfp4", "fp8")
     assert empty["out"].shape == (0, wl.hidden)
+
+
+def test_router_nan_logits_rank_as_minus_infinity():
+    """Reading for non-finite logits (the pages are silent): NaN ranks as
+    -inf.  Brute force over all k-subsets of the logits with NaN replaced
+    by -inf (ties by the smaller index), ids always valid; an all-NaN row
+    selects experts 0..k-1 with NaN weights (softmax of -inf - -inf)."""
+    rng = np.random.default_rng(77)
+    for trial in range(200):
+        e = int(rng.integers(2, 9))
+        k = int(rng.integers(1, e + 1))
+        pool = np.float32([np.nan, -np.inf, -1.0, 0.0, 0.5, 0.5, 2.0])
+        logits = rng.choice(pool, size=(2, e)).astype(np.float32)
+        ids, w = O.route(logits, k)
+        for t in range(2):
+            key = [(-np.inf if np.isnan(x) else float(x)) for x in logits[t]]
+            best = None
+            for sub in itertools.combinations(range(e), k):
+                s = set(sub)
+                if all(key[i] > key[j] or (key[i] == key[j] and i < j)
+                       for i in s for j in range(e) if j not in s):
+                    best = sorted(sub, key=lambda i: (-key[i], i))
+            assert ids[t].tolist() == best
+            if np.isfinite(key[best[0]]):
+                sel = np.array([key[i] for i in best])
+                ref = np.exp(sel - sel[0]) / np.exp(sel - sel[0]).sum()
+                assert np.allclose(w[t], ref, rtol=1e-6, atol=1e-7)
+            else:
+                assert np.all(np.isnan(w[t]))
+    ids, w = O.route(np.full((1, 6), np.nan, np.float32), 3)
+    assert ids[0].tolist() == [0, 1, 2] and np.all(np.isnan(w))
+
+
+def test_finalize_pairs_each_slot_weight_with_its_own_expert_row():
+    """The router-weighted top-k sum (the finalize of the pages'
+    grouped-GEMM + finalize fusion, token_final_scales): with distinct
+    experts and k = 3, out[t] = bf16(sum_j fl32(w_tj * y2_{e_tj}(x_t))) in
+    float32 and slot order, where the weights come from scipy's softmax over
+    the brute-force top-k logits and each (token, expert) MLP is composed
+    here with torch float64 ops on the decoded weights, not through
+    oracle.forward.  Any other pairing of slot weights with expert rows must
+    miss the tolerance, so a pairing error in the oracle fails this test."""
+    T, E, k, H, I = 6, 5, 3, 64, 64
+    wl = MI.small_workload(tokens=T, experts=E, top_k=k, hidden=H, inter=I, seed=41)
+    hb = MI.hidden_bf16(wl.seed, T, H)
+    lg = MI.router_logits(wl.seed, T, E)
+    ex = _make_experts(wl.seed, E, H, I, "mxfp4")
+    r = O.forward(hb, lg, k, lambda e: ex[e], "mxfp4", "fp8")
+
+    # per-token quantised activations, independent of the oracle's quantiser
+    x = torch.from_numpy(F.bf16_to_f32(hb).copy())
+    s = x.abs().amax(dim=1) / 448.0
+    a = torch.from_numpy(F.e4m3_decode(F.e4m3_encode((x / s[:, None]).numpy())))
+
+    def mlp(t, e):
+        w1 = torch.from_numpy(O.layer.decode_weight(ex[e].w1q, ex[e].w1s, "mxfp4"))
+        w2 = torch.from_numpy(O.layer.decode_weight(ex[e].w2q, ex[e].w2s, "mxfp4"))
+        y1 = (torch.matmul(a[t:t + 1], w1.t()) * float(s[t])).float()
+        hh = (torch.nn.functional.silu(y1[:, :I].double()) * y1[:, I:].double()).float()
+        s2 = hh.abs().amax(dim=1) / 448.0
+        a2 = torch.from_numpy(F.e4m3_decode(F.e4m3_encode((hh / s2[:, None]).numpy())))
+        return (torch.matmul(a2, w2.t()) * s2.double()[:, None]).float().numpy()[0]
+
+    sel, wts = [], []
+    for t in range(T):
+        order = sorted(range(E), key=lambda i: (-float(lg[t, i]), i))[:k]
+        sel.append(order)
+        wts.append(scipy.special.softmax(lg[t, order].astype(np.float64)).astype(np.float32))
+    y2 = {(t, j): mlp(t, sel[t][j]) for t in range(T) for j in range(k)}
+    assert len({tuple(v) for v in sel}) > 1 and all(len(set(v)) == k for v in sel)
+
+    def combine(perm):
+        out = np.zeros((T, H), np.float32)
+        for t in range(T):
+            acc = np.zeros(H, np.float32)
+            for j in range(k):
+                acc = (acc + (wts[t][j] * y2[(t, perm[j])]).astype(np.float32)).astype(np.float32)
+            out[t] = acc
+        return F.bf16_rne(out)
+
+    def close(a_bits, b_bits):
+        # torch's silu may differ from the oracle's exp-based one by an ulp
+        d = np.abs(a_bits.astype(np.int64) - b_bits.astype(np.int64))
+        return d.max() <= 1 and np.mean(d == 0) > 0.97
+
+    assert np.array_equal(r["ids"], np.array(sel, np.int32))
+    assert close(r["out"], combine(list(range(k))))
+    for perm in itertools.permutations(range(k)):
+        if list(perm) != list(range(k)):
+            assert not close(r["out"], combine(list(perm))), perm

@@ -99,6 +99,22 @@ def test_int4_invariants():
     assert np.array_equal(s[nz], (amax / np.float32(7))[nz])
 
 
+def test_int4_round_half_even_ties():
+    """INT4 codes round w/s to the nearest integer with ties to even.  Group
+    amax 7 gives s = 7/7 = 1 exactly and amax 3.5 gives s = 0.5, so the
+    quotients below are exact half-integers; the expected codes are written
+    out by hand (round-half-away would give 3, 1, -1, -3, 5, 7, -7)."""
+    w = np.zeros((2, 128), np.float32)
+    w[0, :9] = [7.0, 2.5, 0.5, -0.5, -2.5, 4.5, 6.5, -6.5, 1.5]
+    w[1, :4] = [3.5, 1.25, -0.75, 0.25]          # s = 0.5: 7, 2.5, -1.5, 0.5
+    q, s = Q.int4_quantize(w)
+    assert s[0, 0] == 1.0 and s[1, 0] == 0.5
+    v = F.int4_decode(F.unpack_nibbles(q))
+    assert v[0, :9].tolist() == [7, 2, 0, 0, -2, 4, 6, -6, 2]
+    assert v[1, :4].tolist() == [7, 2, -2, 0]
+    assert np.all(v[0, 9:] == 0) and np.all(v[1, 4:] == 0)
+
+
 def test_token_quant_amax_maps_to_448_for_every_bf16_amax():
     b = np.arange(1, 0x7F80, dtype=np.uint32)  # every positive finite bf16
     amax = (b << 16).view(np.float32)
