@@ -60,6 +60,13 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m mixed_precision_moe_topk_amd.build`")
+        # torch ships its own HIP runtime (soname libamdhip64.so.7, loaded by
+        # torch under the file name libamdhip64.so).  Loaded first, it also
+        # satisfies the library's libamdhip64.so.7 dependency, so the process
+        # has one runtime; the library loaded first would bring the system
+        # runtime and torch a second one, and one of the two would find no
+        # device.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         DP = ctypes.POINTER(Dims)
