@@ -224,6 +224,27 @@ moe_status moe_run(const moe_dims* dims, const void* hidden, int64_t num_tokens,
                    const float* router_logits, const void* weights, const void* scales,
                    int32_t top_k, void* out, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * layer, kernels and results as moe_run_ws, with the workspace taken from a
+ * static device array of MOE_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on every device it runs on until the process ends.  The call
+ * allocates nothing (no hipMalloc / hipFree, no allocating library routine)
+ * and records no stage-trace events.  Every call on one device shares that
+ * device's array, so calls that overlap in time on one device (different
+ * streams or threads without ordering between them) race and corrupt each
+ * other's intermediates; calls ordered on one stream are fine.  The array
+ * needs no clearing: every region is written before it is read within a call.
+ * Arguments as moe_run_ws.  Errors: as moe_run_ws; MOE_ERR_WORKSPACE (nothing
+ * launched) when moe_workspace_query for these dims, num_tokens and top_k
+ * exceeds MOE_NOALLOC_SCRATCH_BYTES — e.g. DeepSeek-V3 shapes (hidden 7168,
+ * inter 2048, top-8) fit up to about 150 tokens; MOE_ERR_HIP if the device
+ * address of the array cannot be looked up. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64ull << 20)
+moe_status moe_run_noalloc(const moe_dims* dims, const void* hidden, int64_t num_tokens,
+                           const float* router_logits, const void* weights, const void* scales,
+                           int32_t top_k, void* out, hipStream_t stream);
+
 /* Frees every workspace moe_run holds (all devices and streams).  Waits for
  * each device that holds one (hipDeviceSynchronize), so no call may be in
  * flight on another thread.  The next moe_run allocates again.  Errors:

@@ -26,7 +26,8 @@ EXPORTS = ("moe_abi_version", "moe_last_error", "moe_weights_query", "moe_prepar
            "moe_unpack_weights", "moe_workspace_query", "moe_workspace_layout", "moe_run_ws",
            "moe_run", "moe_route", "moe_quantize_tokens", "moe_tune_set", "moe_tune_clear",
            "moe_autotune", "moe_trace_enable", "moe_trace_read", "moe_release_arenas",
-           "moe_set_fc2_fused")
+           "moe_set_fc2_fused", "moe_run_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 STAGES = ("route", "quant", "gemm1", "requant", "gemm2", "finalize")
 
 
@@ -80,6 +81,7 @@ def lib():
             "moe_workspace_layout": [DP, I64, I32, ctypes.POINTER(WsLayout)],
             "moe_run_ws": [DP, P, I64, P, P, P, I32, P, P, SZ, P],
             "moe_run": [DP, P, I64, P, P, P, I32, P, P],
+            "moe_run_noalloc": [DP, P, I64, P, P, P, I32, P, P],
             "moe_route": [DP, P, I64, I32, P, P, P, P, P, P, SZ, P],
             "moe_quantize_tokens": [DP, P, I64, P, P, P, P],
             "moe_tune_set": [DP, I64, I32, I32],
@@ -180,6 +182,14 @@ def run(d: LayerDims, hidden, logits, weights, scales, top_k: int, out, stream=N
     T = int(hidden.shape[0])
     _check(lib().moe_run(ctypes.byref(d.c()), _ptr(hidden), T, _ptr(logits), _ptr(weights),
                          _ptr(scales), top_k, _ptr(out), _stream(stream)))
+
+
+def run_noalloc(d: LayerDims, hidden, logits, weights, scales, top_k: int, out, stream=None):
+    """The layer with the library's static device workspace (allocates
+    nothing; workspaces above NOALLOC_SCRATCH_BYTES are refused)."""
+    T = int(hidden.shape[0])
+    _check(lib().moe_run_noalloc(ctypes.byref(d.c()), _ptr(hidden), T, _ptr(logits),
+                                 _ptr(weights), _ptr(scales), top_k, _ptr(out), _stream(stream)))
 
 
 def route(d: LayerDims, logits, top_k: int, ids, weights, expert_offsets, row_token,

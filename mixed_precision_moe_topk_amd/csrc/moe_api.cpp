@@ -422,11 +422,12 @@ moe_status moe_workspace_layout(const moe_dims* dims, int64_t num_tokens, int32_
 
 namespace {
 
-// The layer with tile configuration `force` (< 0: tuned or heuristic).
+// The layer with tile configuration `force` (< 0: tuned or heuristic);
+// trace = false never records stage events (and so never creates any).
 moe_status run_checked(const moe_dims* dims, const void* hidden, int64_t num_tokens,
                        const float* router_logits, const void* weights, const void* scales,
                        int32_t top_k, void* out, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream, int force) {
+                       hipStream_t stream, int force, bool trace = true) {
   moe_ws_layout L;
   MOE_TRY(layout_of(dims, num_tokens, top_k, &L, force));
   if (num_tokens == 0) return ok();
@@ -439,7 +440,7 @@ moe_status run_checked(const moe_dims* dims, const void* hidden, int64_t num_tok
     return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes,
                 L.total);
   MOE_TRY(check_device());
-  TraceCall* tc = tracer().next();
+  TraceCall* tc = trace ? tracer().next() : nullptr;
   trace_mark(tc, 0, stream);
 
   const Sizes s = sizes_of(dims);
@@ -598,6 +599,20 @@ struct TuneScratch {
 };
 
 }  // namespace
+
+namespace moe {
+// moe_run_ws without stage tracing, for the entry point that must not
+// allocate (moe_noalloc.hip); same validation and kernels.
+moe_status run_ws_untraced(const moe_dims* dims, const void* hidden, int64_t num_tokens,
+                           const float* router_logits, const void* weights, const void* scales,
+                           int32_t top_k, void* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  return run_checked(dims, hidden, num_tokens, router_logits, weights, scales, top_k, out,
+                     workspace, workspace_bytes, stream, -1, false);
+}
+// Records a failure of the calling thread for moe_last_error.
+moe_status set_error(moe_status st, const char* msg) { return fail(st, "%s", msg); }
+}  // namespace moe
 
 extern "C" {
 
