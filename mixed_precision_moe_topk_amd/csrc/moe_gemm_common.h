@@ -311,6 +311,182 @@ __device__ __forceinline__ void finish_tile(const GemmParams& p, const v4f (&acc
   epilogue<FC1, WM, WN, RS>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Transposed accumulators.  For every format except INT4 the kernels give the
+// matrix core the weights as its A operand and the activations as B, which
+// computes the transpose of the output tile: lane l of tile (i, j) then holds
+// columns 16 (nb0 + j) + 4 (l / 16) + [0, 4) of the single row
+// row_base + RS i + l % 16.  Four consecutive columns of one row make one
+// 16-byte store, so the epilogue issues a quarter of the store instructions of
+// the row-per-register layout above (which INT4 keeps: its post-MMA group
+// scale is per output column, one per lane there), and a lane needs one row
+// scale per subtile instead of four.  Both operand layouts are the same for
+// rows and columns (lane l holds row / column l % 16 and the same K range), so
+// only the argument order and the scale operands swap.
+template <int AF, int SW, int SA>
+__device__ __forceinline__ v4f mfma_wt(const v8i& w, const v8i& a, const v4f& c, int scale_w,
+                                       int scale_a) {
+  // D^T = W . A^T: weights E2M1 (format 4) with their E8M0 scale word and
+  // byte select SW; activations in format AF with scale word / byte select SA
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, a, c, 4, AF, SW, scale_w, SA, scale_a);
+}
+
+// Row scale of this lane's row in each subtile (1 without row scales).
+template <bool FC1, int WM, int RS = 16>
+__device__ __forceinline__ void load_row_scales_t(const GemmParams& p, int row_base, int row_end,
+                                                  int lane, float (&sc)[WM]) {
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+    const int r = min(row_base + RS * i + (lane & 15), row_end - 1);
+    sc[i] = !p.row_scale ? 1.0f : FC1 ? p.row_scale[p.row_token[r]] : p.row_scale[r];
+  }
+}
+
+__device__ __forceinline__ void store4_nt(float* dst, float x, float y, float z, float w) {
+  __builtin_nontemporal_store(v4f{x, y, z, w}, reinterpret_cast<v4f*>(dst));
+}
+
+// FC1: h = silu(g * s) * (u * s) for tiles (2q, 2q+1) = gate / up of
+// intermediate block (nb0 + 2q) / 2; FC2: y2 = acc * s.  Streaming stores.
+template <bool FC1, int WM, int WN, int RS = 16>
+__device__ __forceinline__ void epilogue_t(const GemmParams& p, const v4f (&acc)[WM][WN],
+                                           const float (&sc)[WM], int row_base, int row_end,
+                                           int nvalid, int64_t nb0, int jvalid, int lane) {
+  const int c4 = 4 * (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+    if (i >= nvalid) continue;
+    const int r = row_base + RS * i + (lane & 15);
+    if (r >= row_end) continue;
+    float* orow = p.out + (int64_t)r * p.out_stride;
+    const float s = sc[i];
+    if (FC1) {
+#pragma unroll
+      for (int q = 0; q < WN / 2; ++q) {
+        if (2 * q >= jvalid) continue;
+        const int64_t c = ((nb0 + 2 * q) >> 1) * 16 + c4;
+        const v4f g = acc[i][2 * q], u = acc[i][2 * q + 1];
+        store4_nt(orow + c, silu(g[0] * s) * (u[0] * s), silu(g[1] * s) * (u[1] * s),
+                  silu(g[2] * s) * (u[2] * s), silu(g[3] * s) * (u[3] * s));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        if (j >= jvalid) continue;
+        const v4f a = acc[i][j];
+        store4_nt(orow + (nb0 + j) * 16 + c4, a[0] * s, a[1] * s, a[2] * s, a[3] * s);
+      }
+    }
+  }
+}
+
+// FC1 epilogue for MX activation formats, transposed layout: MX block
+// b = nb0 / 4 + m covers intermediate blocks 2m, 2m+1 of the wave (device
+// tiles 4m .. 4m+3); lane l holds its row's columns 4 (l/16) + [0, 4) of both
+// halves, so the block amax is a reduction over the four lanes l % 16 + 16 g.
+// Same h values, exponent rule and encoders as the separate FC2 quantiser.
+template <bool E2M1, int WM, int WN, int RS = 16>
+__device__ __forceinline__ void epilogue_fc1_mx_t(const GemmParams& p, const v4f (&acc)[WM][WN],
+                                                  int row_base, int row_end, int nvalid,
+                                                  int64_t nb0, int jvalid, int lane) {
+  static_assert(WN % 4 == 0, "whole 32-column MX blocks per wave");
+  if (jvalid < WN) return;  // columns past N (N is a multiple of 256)
+  const int g4 = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+    if (i >= nvalid) continue;
+    const int r = row_base + RS * i + (lane & 15);
+    const bool live = r < row_end;
+    uint8_t* qrow = p.q_out + (int64_t)r * p.q_stride;
+#pragma unroll
+    for (int m = 0; m < WN / 4; ++m) {
+      const int64_t b = (nb0 >> 2) + m;  // MX block: h columns [32b, 32b + 32)
+      float x0[4], x1[4];
+      float amax = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        x0[v] = silu(acc[i][4 * m][v]) * acc[i][4 * m + 1][v];
+        x1[v] = silu(acc[i][4 * m + 2][v]) * acc[i][4 * m + 3][v];
+        amax = fmaxf(amax, fmaxf(fabsf(x0[v]), fabsf(x1[v])));
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      const int x = mx_exponent<E2M1 ? 2 : 8>(amax);
+      const float inv = __uint_as_float((uint32_t)(127 - x) << 23);  // 2^-X
+      if (E2M1) {
+        uint32_t n0 = 0, n1 = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          n0 |= (e2m1_magnitude_code(fabsf(x0[v]) * inv) | ((__float_as_uint(x0[v]) >> 31) << 3)) << (4 * v);
+          n1 |= (e2m1_magnitude_code(fabsf(x1[v]) * inv) | ((__float_as_uint(x1[v]) >> 31) << 3)) << (4 * v);
+        }
+        if (live) {  // columns 32b + 4g + v -> byte 16b + 2g (+ 8 for the second half)
+          *reinterpret_cast<uint16_t*>(qrow + 16 * b + 2 * g4) = (uint16_t)n0;
+          *reinterpret_cast<uint16_t*>(qrow + 16 * b + 8 + 2 * g4) = (uint16_t)n1;
+        }
+      } else if (live) {
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          w0 |= e4m3_encode(x0[v] * inv) << (8 * v);
+          w1 |= e4m3_encode(x1[v] * inv) << (8 * v);
+        }
+        *reinterpret_cast<uint32_t*>(qrow + 32 * b + 4 * g4) = w0;
+        *reinterpret_cast<uint32_t*>(qrow + 32 * b + 16 + 4 * g4) = w1;
+      }
+      if (live && g4 == 0)
+        p.q_bscales[(int64_t)r * p.q_bstride + mx_scale_offset(b)] = (uint8_t)(x + 127);
+    }
+  }
+}
+
+// FC1 epilogue for BF16 activations, transposed layout: bf16(h) of the
+// lane's four columns, one 8-byte store.
+template <int WM, int WN, int RS = 16>
+__device__ __forceinline__ void epilogue_fc1_bf16_t(const GemmParams& p, const v4f (&acc)[WM][WN],
+                                                    int row_base, int row_end, int nvalid,
+                                                    int64_t nb0, int jvalid, int lane) {
+  const int c4 = 4 * (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+    if (i >= nvalid) continue;
+    const int r = row_base + RS * i + (lane & 15);
+    if (r >= row_end) continue;
+    uint16_t* qrow = reinterpret_cast<uint16_t*>(p.q_out + (int64_t)r * p.q_stride);
+#pragma unroll
+    for (int q = 0; q < WN / 2; ++q) {
+      if (2 * q >= jvalid) continue;
+      const int64_t c = ((nb0 + 2 * q) >> 1) * 16 + c4;
+      uint32_t h[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) h[v] = bf16_bits(silu(acc[i][2 * q][v]) * acc[i][2 * q + 1][v]);
+      *reinterpret_cast<uint2*>(qrow + c) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    }
+  }
+}
+
+// End of a GEMM block with transposed accumulators: the fused FC1 + FC2-input
+// epilogue when the caller asks for it (q_out set) and the format and tile
+// allow it, else the plain one with the given row scales.
+template <int V, bool FC1, int WM, int WN, int RS = 16>
+__device__ __forceinline__ void finish_tile_t(const GemmParams& p, const v4f (&acc)[WM][WN],
+                                              const float (&sc)[WM], int row_base, int row_end,
+                                              int nvalid, int64_t nb0, int jvalid, int lane) {
+  if constexpr (FC1 && a_blockscaled(V) && WN % 4 == 0) {
+    if (p.q_out) {
+      epilogue_fc1_mx_t<a_fp4(V), WM, WN, RS>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+      return;
+    }
+  }
+  if constexpr (FC1 && V == kMxfp4Bf16) {
+    if (p.q_out) {
+      epilogue_fc1_bf16_t<WM, WN, RS>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+      return;
+    }
+  }
+  epilogue_t<FC1, WM, WN, RS>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
+}
+
 hipError_t launch_gemm_direct(int variant, bool fc1, int cfg, const GemmParams& p,
                               int64_t max_tiles, hipStream_t st);
 hipError_t launch_gemm_lds(int variant, bool fc1, int cfg, const GemmParams& p,

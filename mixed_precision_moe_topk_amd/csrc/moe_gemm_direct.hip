@@ -8,7 +8,8 @@
 namespace moe {
 
 // Block = 4 waves, WAVES_M x (4 / WAVES_M); each wave owns WM x WN 16x16
-// output tiles.
+// output tiles (transposed accumulators, weights as the MFMA's A operand,
+// except for INT4: see moe_gemm_common.h).
 template <int V, bool FC1, int WAVES_M, int WM, int WN>
 __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   constexpr int WAVES_N = 4 / WAVES_M;
@@ -118,11 +119,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
 #pragma unroll
           for (int j = 0; j < WN; ++j) {
             if (j >= jvalid) continue;
+            // weights as the MFMA's A operand: transposed accumulators
             switch (ks & 3) {
-              case 0: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], AF, 4, 0, sa, 0, (int)sc[j]); break;
-              case 1: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], AF, 4, MXA ? 1 : 0, sa, 1, (int)sc[j]); break;
-              case 2: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], AF, 4, MXA ? 2 : 0, sa, 2, (int)sc[j]); break;
-              default: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], acc[i][j], AF, 4, MXA ? 3 : 0, sa, 3, (int)sc[j]); break;
+              case 0: acc[i][j] = mfma_wt<AF, 0, 0>(bop[j], aop, acc[i][j], (int)sc[j], sa); break;
+              case 1: acc[i][j] = mfma_wt<AF, 1, MXA ? 1 : 0>(bop[j], aop, acc[i][j], (int)sc[j], sa); break;
+              case 2: acc[i][j] = mfma_wt<AF, 2, MXA ? 2 : 0>(bop[j], aop, acc[i][j], (int)sc[j], sa); break;
+              default: acc[i][j] = mfma_wt<AF, 3, MXA ? 3 : 0>(bop[j], aop, acc[i][j], (int)sc[j], sa); break;
             }
           }
         }
@@ -157,8 +159,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
           const v8bf bop = fp4x8_to_bf16(bw[s], scale);
 #pragma unroll
           for (int i = 0; i < WM; ++i) {
-            if (i < nvalid)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[i][s]), bop,
+            if (i < nvalid)  // weights as the A operand: transposed accumulators
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop, as_bf16x8(a[i][s]),
                                                                   acc[i][j], 0, 0, 0);
           }
         }
@@ -199,7 +201,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     if (ks < KS) compute(ks, ac, bc, scc, asc);
   }
 
-  finish_tile<V, FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  if constexpr (V == kInt4Fp8) {
+    finish_tile<V, FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  } else {
+    float sc[WM];
+    load_row_scales_t<FC1, WM>(p, row_base, row_end, lane, sc);
+    finish_tile_t<V, FC1, WM, WN>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  }
 }
 
 

@@ -135,10 +135,18 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   // per-token E4M3: row scales loaded before the K loop (their latency is
-  // then not paid between the last MFMA and the first output store)
-  constexpr bool PRE_SC = V == kMxfp4Fp8 || V == kInt4Fp8;
+  // then not paid between the last MFMA and the first output store).  MXFP4
+  // weights: transposed accumulators (weights as the MFMA's A operand), one
+  // row scale per subtile; INT4: row-per-register accumulators, four
+  constexpr bool TR = MX;
   float sc[WM][4];
-  if constexpr (PRE_SC) load_row_scales<FC1, WM>(p, row_base, row_end, lane, sc);
+  float sct[WM];
+  if constexpr (V == kInt4Fp8) load_row_scales<FC1, WM>(p, row_base, row_end, lane, sc);
+  if constexpr (V == kMxfp4Fp8) load_row_scales_t<FC1, WM>(p, row_base, row_end, lane, sct);
+  if constexpr (TR && V != kMxfp4Fp8) {
+#pragma unroll
+    for (int i = 0; i < WM; ++i) sct[i] = 1.0f;
+  }
 
   v4u ast[AS][NCH];
   uint4 bq[NB][WN];
@@ -232,9 +240,9 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
         }
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
-          if (MX) {
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                aop, bop[j], acc[i][j], AF, 4, MXA ? S : 0, MXA ? (int)ax[i] : 127, S, (int)sx[j]);
+          if constexpr (MX) {
+            acc[i][j] = mfma_wt<AF, S, MXA ? S : 0>(bop[j], aop, acc[i][j], (int)sx[j],
+                                                   MXA ? (int)ax[i] : 127);
           } else {
             const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 aop, bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
@@ -285,10 +293,10 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
   if (ks < KS) step(std::integral_constant<int, 0>{}, ks);
   if (ks + 1 < KS) step(std::integral_constant<int, 1>{}, ks + 1);
   if (ks + 2 < KS) step(std::integral_constant<int, 2>{}, ks + 2);
-  if constexpr (PRE_SC)
-    epilogue_sc<FC1, WM, WN>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  if constexpr (TR)
+    finish_tile_t<V, FC1, WM, WN>(p, acc, sct, row_base, row_end, nvalid, nb0, jvalid, lane);
   else
-    finish_tile<V, FC1, WM, WN>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+    epilogue_sc<FC1, WM, WN>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
 template <int V, bool FC1, int NW, int WAVES_M, int WM, int WN, int MINB = 2, int PB = 2,
@@ -706,9 +714,14 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
     for (int j = 0; j < WN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   // per-token E4M3: the row scales are loaded before the K loop, so their
   // latency (two dependent loads through row_token for GEMM1) is not paid
-  // between the last MFMA and the first output store
-  float sc[WM][4];
-  if constexpr (!MXA) load_row_scales<FC1, WM, RS>(p, row_base, row_end, lane, sc);
+  // between the last MFMA and the first output store; with the transposed
+  // accumulators a lane holds one row per subtile, so one scale each
+  float sc[WM];
+  if constexpr (!MXA) load_row_scales_t<FC1, WM, RS>(p, row_base, row_end, lane, sc);
+  else {
+#pragma unroll
+    for (int i = 0; i < WM; ++i) sc[i] = 1.0f;
+  }
   uint32_t sx[WN];
   uint4 bq[WN];          // weight fragments (the E2M1 operand is built at each MFMA)
   uint4 alo[2], ahi[2];  // A fragment halves, two subtiles in flight
@@ -780,8 +793,8 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
           const int ax = MXA ? axr[(P0 + i) & 1] : 127;
 #pragma unroll
           for (int j = 0; j < WN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                aop, fp4_operand(bq[j]), acc[i][j], AF, 4, MXA ? S : 0, ax, S, (int)sx[j]);
+            acc[i][j] = mfma_wt<AF, S, MXA ? S : 0>(fp4_operand(bq[j]), aop, acc[i][j],
+                                                   (int)sx[j], ax);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (i < 4) issue_part(i);
@@ -801,8 +814,8 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         if (last)
-          acc[IL][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              aop, fp4_operand(bq[j]), acc[IL][j], AF, 4, MXA ? S : 0, ax, S, (int)sx[j]);
+          acc[IL][j] = mfma_wt<AF, S, MXA ? S : 0>(fp4_operand(bq[j]), aop, acc[IL][j],
+                                                  (int)sx[j], ax);
         bq[j] = *reinterpret_cast<const uint4*>(bn + j * 1024);
         if constexpr (S == 3) sx[j] = *reinterpret_cast<const uint32_t*>(sn + j * 256);
         __builtin_amdgcn_sched_barrier(0);
@@ -842,8 +855,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
             const v8i aop = as_v8i(alo[i & 1], ahi[i & 1]);
 #pragma unroll
             for (int j = 0; j < WN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  aop, bop[j], acc[i][j], AF, 4, S, axr[i & 1], S, (int)sx[j]);
+              acc[i][j] = mfma_wt<AF, S, S>(bop[j], aop, acc[i][j], (int)sx[j], axr[i & 1]);
           }
           __builtin_amdgcn_sched_barrier(0);
           issue_part(i);
@@ -872,8 +884,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
             const int ax = MXA ? *reinterpret_cast<const int*>(sa + i * kSaSub) : 127;
 #pragma unroll
             for (int j = 0; j < WN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  aop, bop[j], acc[i][j], AF, 4, MXA ? S : 0, ax, S, (int)sx[j]);
+              acc[i][j] = mfma_wt<AF, S, MXA ? S : 0>(bop[j], aop, acc[i][j], (int)sx[j], ax);
           }
           __builtin_amdgcn_sched_barrier(0);
           issue_part(i);
@@ -921,10 +932,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   if (ks + 1 < KS) { step(std::integral_constant<int, 1>{}, ks + 1, bstage); bstage = bstage == 2 ? 0 : bstage + 1; }
   if (ks + 2 < KS) step(std::integral_constant<int, 2>{}, ks + 2, bstage);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if constexpr (!MXA)
-    epilogue_sc<FC1, WM, WN, RS>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
-  else
-    finish_tile<V, FC1, WM, WN, RS>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  finish_tile_t<V, FC1, WM, WN, RS>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
 template <int V, bool FC1, int WM>
