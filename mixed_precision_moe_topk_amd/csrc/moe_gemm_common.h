@@ -126,12 +126,12 @@ __device__ __forceinline__ float silu(float g) {
 //   FC1: tiles (2q, 2q+1) are the gate and up halves of intermediate block
 //        (nb0 + 2q)/2; h = silu(g*s) * (u*s), s = token scale.
 //   FC2: y2 = acc * s, s = row scale.
-// The outputs are written with streaming (non-temporal) stores: h and y2 are
-// read once, by the next kernel, long after the block is gone, and keeping
-// them out of the caches measured 1-4 % faster on the prefill GEMM2 and
-// finalize (an L2-resident y2 for a fused finalize by float atomics, tried
-// as well, made GEMM2 2.1x slower).  epilogue_sc takes the row scales
-// loaded beforehand (load_row_scales), epilogue loads them itself.
+// These row-per-register epilogues (INT4 only) write with streaming
+// (non-temporal) 4-byte stores: h and y2 are read once, by the next kernel,
+// long after the block is gone, and keeping them out of the caches measured
+// 1-4 % faster there (an L2-resident y2 for a fused finalize by float
+// atomics, tried as well, made GEMM2 2.1x slower).  epilogue_sc takes the
+// row scales loaded beforehand (load_row_scales), epilogue loads them itself.
 
 // Row scales of this lane's accumulator rows (1 without row scales).
 template <bool FC1, int WM, int RS = 16>
@@ -206,108 +206,12 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const v4f (&acc)[W
   epilogue_sc<FC1, WM, WN, RS>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
-// FC1 epilogue for MX activation formats that quantises the FC2 input in
-// place of writing h.  Intermediate blocks (2m, 2m+1) of a wave are the 32
-// columns of MX block nb0/4 + m (the wave's first device column block nb0 is a
-// multiple of 4 when WN % 4 == 0); lane l holds column l%16 of both halves for
-// rows 4(l/16) + v, so the block amax is a reduction over the 16 lanes of a
-// row group.  The h values, the exponent rule and the encoders are the ones
-// the separate FC2 quantiser uses, so the codes are the same bits.  Row
-// scales are 1 for these formats (the caller passes none).
-template <bool E2M1, int WM, int WN, int RS = 16>
-__device__ __forceinline__ void epilogue_fc1_mx(const GemmParams& p, const v4f (&acc)[WM][WN],
-                                                int row_base, int row_end, int nvalid,
-                                                int64_t nb0, int jvalid, int lane) {
-  static_assert(WN % 4 == 0, "whole 32-column MX blocks per wave");
-  if (jvalid < WN) return;  // columns past N (N is a multiple of 256)
-  const int col_lane = lane & 15;
-  const int row_lane = 4 * (lane >> 4);
-#pragma unroll
-  for (int m = 0; m < WN / 4; ++m) {
-    const int64_t b = (nb0 >> 2) + m;  // MX block: h columns [32b, 32b + 32)
-#pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      if (i >= nvalid) continue;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = row_base + RS * i + row_lane + v;
-        const float x0 = silu(acc[i][4 * m][v]) * acc[i][4 * m + 1][v];
-        const float x1 = silu(acc[i][4 * m + 2][v]) * acc[i][4 * m + 3][v];
-        float amax = fmaxf(fabsf(x0), fabsf(x1));
-        amax = fmaxf(amax, __shfl_xor(amax, 1));
-        amax = fmaxf(amax, __shfl_xor(amax, 2));
-        amax = fmaxf(amax, __shfl_xor(amax, 4));
-        amax = fmaxf(amax, __shfl_xor(amax, 8));
-        const int x = mx_exponent<E2M1 ? 2 : 8>(amax);
-        const float inv = __uint_as_float((uint32_t)(127 - x) << 23);  // 2^-X
-        uint8_t* qrow = p.q_out + (int64_t)r * p.q_stride;
-        if (E2M1) {
-          const uint32_t n0 = e2m1_magnitude_code(fabsf(x0) * inv) | ((__float_as_uint(x0) >> 31) << 3);
-          const uint32_t n1 = e2m1_magnitude_code(fabsf(x1) * inv) | ((__float_as_uint(x1) >> 31) << 3);
-          const uint32_t o0 = __shfl_xor(n0, 1), o1 = __shfl_xor(n1, 1);  // odd column's nibble
-          if (r < row_end && !(col_lane & 1)) {
-            qrow[16 * b + col_lane / 2] = (uint8_t)(n0 | (o0 << 4));
-            qrow[16 * b + 8 + col_lane / 2] = (uint8_t)(n1 | (o1 << 4));
-          }
-        } else if (r < row_end) {
-          qrow[32 * b + col_lane] = (uint8_t)e4m3_encode(x0 * inv);
-          qrow[32 * b + 16 + col_lane] = (uint8_t)e4m3_encode(x1 * inv);
-        }
-        if (r < row_end && col_lane == 0)
-          p.q_bscales[(int64_t)r * p.q_bstride + mx_scale_offset(b)] = (uint8_t)(x + 127);
-      }
-    }
-  }
-}
-
-// FC1 epilogue for BF16 activations: the FC2 input is bf16(h) element by
-// element (no row scale), so GEMM1 writes those bits (q_out, q_stride bytes
-// per row) in place of h: the same h value and rounding as the separate
-// conversion, without the float32 round trip.
-template <int WM, int WN, int RS = 16>
-__device__ __forceinline__ void epilogue_fc1_bf16(const GemmParams& p, const v4f (&acc)[WM][WN],
-                                                  int row_base, int row_end, int nvalid,
-                                                  int64_t nb0, int jvalid, int lane) {
-  const int col_lane = lane & 15;
-  const int row_lane = 4 * (lane >> 4);
-#pragma unroll
-  for (int q = 0; q < WN / 2; ++q) {
-    if (2 * q >= jvalid) continue;
-    const int64_t c = ((nb0 + 2 * q) >> 1) * 16 + col_lane;
-#pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      if (i >= nvalid) continue;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = row_base + RS * i + row_lane + v;
-        if (r < row_end) {
-          const float h = silu(acc[i][2 * q][v]) * acc[i][2 * q + 1][v];
-          reinterpret_cast<uint16_t*>(p.q_out + (int64_t)r * p.q_stride)[c] = (uint16_t)bf16_bits(h);
-        }
-      }
-    }
-  }
-}
-
-// End of a GEMM block: the fused FC1 + FC2-input epilogue when the caller
-// asks for it (q_out set) and the format and tile allow it, else the plain
-// epilogue.
+// End of a GEMM block with row-per-register accumulators (INT4 weights).
 template <int V, bool FC1, int WM, int WN, int RS = 16>
 __device__ __forceinline__ void finish_tile(const GemmParams& p, const v4f (&acc)[WM][WN],
                                             int row_base, int row_end, int nvalid, int64_t nb0,
                                             int jvalid, int lane) {
-  if constexpr (FC1 && a_blockscaled(V) && WN % 4 == 0) {
-    if (p.q_out) {
-      epilogue_fc1_mx<a_fp4(V), WM, WN, RS>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
-      return;
-    }
-  }
-  if constexpr (FC1 && V == kMxfp4Bf16) {
-    if (p.q_out) {
-      epilogue_fc1_bf16<WM, WN, RS>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
-      return;
-    }
-  }
+  static_assert(V == kInt4Fp8, "the other formats use transposed accumulators");
   epilogue<FC1, WM, WN, RS>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
@@ -345,9 +249,15 @@ __device__ __forceinline__ void load_row_scales_t(const GemmParams& p, int row_b
 __device__ __forceinline__ void store4_nt(float* dst, float x, float y, float z, float w) {
   __builtin_nontemporal_store(v4f{x, y, z, w}, reinterpret_cast<v4f*>(dst));
 }
+__device__ __forceinline__ void store4(float* dst, float x, float y, float z, float w) {
+  *reinterpret_cast<v4f*>(dst) = v4f{x, y, z, w};
+}
 
 // FC1: h = silu(g * s) * (u * s) for tiles (2q, 2q+1) = gate / up of
-// intermediate block (nb0 + 2q) / 2; FC2: y2 = acc * s.  Streaming stores.
+// intermediate block (nb0 + 2q) / 2, streaming stores; FC2: y2 = acc * s,
+// plain (cached) stores.  Same-box timings of the prefill GEMMs with 16-byte
+// stores: plain y2 stores made GEMM2 6 % faster on both DeepSeek prefill
+// shapes, plain h stores made the 4096-token GEMM1 6 % slower.
 template <bool FC1, int WM, int WN, int RS = 16>
 __device__ __forceinline__ void epilogue_t(const GemmParams& p, const v4f (&acc)[WM][WN],
                                            const float (&sc)[WM], int row_base, int row_end,
@@ -374,7 +284,7 @@ __device__ __forceinline__ void epilogue_t(const GemmParams& p, const v4f (&acc)
       for (int j = 0; j < WN; ++j) {
         if (j >= jvalid) continue;
         const v4f a = acc[i][j];
-        store4_nt(orow + (nb0 + j) * 16 + c4, a[0] * s, a[1] * s, a[2] * s, a[3] * s);
+        store4(orow + (nb0 + j) * 16 + c4, a[0] * s, a[1] * s, a[2] * s, a[3] * s);
       }
     }
   }

@@ -329,7 +329,8 @@ __device__ __forceinline__ void interleave_schedule_ab() {
 }
 
 // ----------------------------------------------------------------------------
-// Grouped GEMM with both operands staged through LDS (E4M3 activations).
+// Grouped GEMM with both operands staged through LDS (INT4 weights x E4M3
+// activations, 128-row tiles).
 // Block = NW waves, WAVES_M x WAVES_N, each wave 16*WM rows x 16*WN device
 // columns; block tile BM x BN.  A per-thread global load carries at most one
 // 16-byte chunk of the step's A tile or weight tile, so every weight byte
@@ -340,12 +341,11 @@ __device__ __forceinline__ void interleave_schedule_ab() {
 // block's weight fragments in their device order (16-column block b at
 // b * 1 KB, lane l's 16 bytes at l * 16: reads and writes are conflict-free).
 // Two stages, one barrier per step; global loads run two steps ahead through
-// two register staging sets.  MXFP4 scale words (one per four steps) and INT4
-// group scales go straight to registers.
+// two register staging sets.  The group scales go straight to registers.
 template <int V, bool FC1, int NW, int WAVES_M, int WM, int WN, bool FULL>
 __device__ __forceinline__ void gemm_ab_body(const GemmParams& p, uint8_t* lds, const Tile tile,
                                              const int nt) {
-  static_assert(V == kMxfp4Fp8 || V == kInt4Fp8, "E4M3 activations only");
+  static_assert(V == kInt4Fp8, "INT4 weights x E4M3 activations");
   static_assert(!FC1 || WN % 2 == 0, "FC1 pairs gate/up tiles");
   constexpr int NT = kWave * NW;
   constexpr int WAVES_N = NW / WAVES_M;
@@ -357,7 +357,6 @@ __device__ __forceinline__ void gemm_ab_body(const GemmParams& p, uint8_t* lds, 
   constexpr int NCB = BNB * 64 / NT;       // weight chunks per thread per step
   static_assert(NCA * NT == BM * 8 && NCB * NT == BNB * 64, "chunks must split evenly");
   static_assert(128 % (16 * WN) == 0, "wave columns must tile 128");
-  constexpr bool MX = V == kMxfp4Fp8;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = lane_id();
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -366,7 +365,7 @@ __device__ __forceinline__ void gemm_ab_body(const GemmParams& p, uint8_t* lds, 
   const int nvalid = __builtin_amdgcn_readfirstlane(max(0, min(WM, (row_end - row_base + 15) / 16)));
 
   const int K = p.K;
-  const int KS = K / kKStep, KS4 = (KS + 3) / 4;
+  const int KS = K / kKStep;
   const int64_t e = tile.expert;
   const uint8_t* wbase = p.w + e * p.w_expert_stride;
   const uint8_t* sbase = p.s + e * p.s_expert_stride;
@@ -386,9 +385,7 @@ __device__ __forceinline__ void gemm_ab_body(const GemmParams& p, uint8_t* lds, 
     const int rr = min(tile.row0 + r, row_end - 1);
     const int64_t src = FC1 ? (int64_t)p.row_token[rr] : (int64_t)rr;
     asrc[u] = p.a + src * p.a_stride + 16 * c;
-    int g, h;
-    if (MX) { g = c & 3; h = c >> 2; }
-    else { g = c >> 1; h = c & 1; }
+    const int g = c >> 1, h = c & 1;  // k = 32g + 16h + [0,16)
     const int rho = r & 15;
     adst[u] = ((r >> 4) * 2 + h) * 1024 + (16 * g + (rho ^ ((2 * g + h) | ((rho & 1) << 3)))) * 16;
   }
@@ -413,8 +410,7 @@ __device__ __forceinline__ void gemm_ab_body(const GemmParams& p, uint8_t* lds, 
     for (int j = 0; j < WN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   v4u ast[2][NCA], bst[2][NCB];
-  uint32_t sq[4][WN];            // INT4 group scales of steps ks .. ks+3 (mod 4)
-  uint32_t sx[WN], sx_next[WN];  // MXFP4 scale words of this / the next 4 steps
+  uint32_t sq[4][WN];  // group scales of steps ks .. ks+3 (mod 4)
 
   auto load_ab = [&](int ks, v4u (&da)[NCA], v4u (&db)[NCB]) __attribute__((always_inline)) {
 #pragma unroll
@@ -436,31 +432,17 @@ __device__ __forceinline__ void gemm_ab_body(const GemmParams& p, uint8_t* lds, 
       sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS + ks) * 16 + (lane & 15)) * 4);
     }
   };
-  auto load_sx = [&](int ks, uint32_t (&sc)[WN]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < WN; ++j) {
-      const int64_t nb = min(nb0 + j, nb_last);
-      sc[j] = *reinterpret_cast<const uint32_t*>(sbase + ((nb * KS4 + (ks >> 2)) * 64 + lane) * 4);
-    }
-  };
-
   auto step = [&](auto s_c, int ks) __attribute__((always_inline)) {
     constexpr int S = decltype(s_c)::value;
-    if constexpr (MX && S == 0) {
-#pragma unroll
-      for (int j = 0; j < WN; ++j) sx[j] = sx_next[j];
-    }
     const int kp = min(ks + 2, KS - 1);
     load_ab(kp, ast[S & 1], bst[S & 1]);
-    if constexpr (!MX) load_sq(kp, sq[(S + 2) % 4]);
-    constexpr bool LOAD_SX = MX && (S + 2) % 4 == 0;
-    if constexpr (LOAD_SX) load_sx(kp, sx_next);
+    load_sq(kp, sq[(S + 2) % 4]);
     const uint8_t* sbuf = lds + (S & 1) * SBUF;
     v8i bop[WN];
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
       const uint4 b = *reinterpret_cast<const uint4*>(sbuf + rdb + j * 1024);
-      bop[j] = MX ? fp4_operand(b) : int4_operand(b);
+      bop[j] = int4_operand(b);
     }
     const uint8_t* abuf = sbuf + (WM * wm) * 2048;
 #pragma unroll
@@ -471,22 +453,15 @@ __device__ __forceinline__ void gemm_ab_body(const GemmParams& p, uint8_t* lds, 
         const v8i aop = as_v8i(lo, hi);
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
-          if (MX) {
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                aop, bop[j], acc[i][j], 0, 4, 0, 127, S, (int)sx[j]);
-          } else {
-            const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                aop, bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-            const float gs = __uint_as_float(sq[S][j]);
+          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              aop, bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+          const float gs = __uint_as_float(sq[S][j]);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[i][j][v] += part[v] * gs;
-          }
+          for (int v = 0; v < 4; ++v) acc[i][j][v] += part[v] * gs;
         }
       }
     }
-    if (FULL)
-      interleave_schedule_ab<WM * WN, NCA + NCB + (MX ? (LOAD_SX ? WN : 0) : WN), WN + 2,
-                             2 * WM - 2>();
+    if (FULL) interleave_schedule_ab<WM * WN, NCA + NCB + WN, WN + 2, 2 * WM - 2>();
     __builtin_amdgcn_sched_barrier(0);
     // operands of step ks+1 (harmless copies of the last step once past the end)
     store_ab((S + 1) & 1, ast[(S + 1) & 1], bst[(S + 1) & 1]);
@@ -495,11 +470,10 @@ __device__ __forceinline__ void gemm_ab_body(const GemmParams& p, uint8_t* lds, 
 
   // prologue loads in step order (fenced: see gemm_lds_body)
   load_ab(0, ast[0], bst[0]);
-  if (MX) load_sx(0, sx_next);
-  else load_sq(0, sq[0]);
+  load_sq(0, sq[0]);
   __builtin_amdgcn_sched_barrier(0);
   load_ab(min(1, KS - 1), ast[1], bst[1]);
-  if (!MX) load_sq(min(1, KS - 1), sq[1]);
+  load_sq(min(1, KS - 1), sq[1]);
   __builtin_amdgcn_sched_barrier(0);
   store_ab(0, ast[0], bst[0]);
   __syncthreads();
