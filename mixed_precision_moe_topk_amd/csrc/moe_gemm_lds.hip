@@ -807,14 +807,19 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
       const uint8_t* sa = sa_at(ks);
       const uint8_t* as = a_at(S & 1);
       v8i bop[WN];
-      if constexpr (MXA && !A4) {
-        // MXFP8 GEMM1: LDS reads in MFMA order, the A fragment and scale of
-        // subtile 0 and the weight fragments first, then those of subtile
-        // i + 1 while the MFMAs of subtile i run.  Only two A fragments are
-        // live at a time, which leaves the registers for the activation
-        // scales in the 160-row tile.  The reads are unconditional
+      if constexpr (!A4) {
+        // GEMM1 with E4M3 codes (per-token or MXFP8): LDS reads in MFMA
+        // order, the A fragment (and MXFP8 scale) of subtile 0 and the weight
+        // fragments first, then those of subtile i + 1 while the MFMAs of
+        // subtile i run, so a subtile's MFMAs do not wait for its own reads.
+        // Only two A fragments are live at a time (the MXFP8 activation
+        // scales fit in the 160-row tile).  The reads are unconditional
         // (subtiles past the tile end hold copies of its last row); only the
-        // MFMAs of such subtiles are skipped.
+        // MFMAs of such subtiles are skipped.  For per-token E4M3 this order
+        // was 2-4 % slower than the compiler's own while the row-per-register
+        // epilogue's scales took 20 registers; with transposed accumulators
+        // (5 scales) it is 2.8 % faster on the 16384-token DeepSeek-V4-Pro
+        // GEMM1 (3.38 -> 3.29 ms, same box).
         read_a(as, sa, 0, 0);
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
@@ -829,16 +834,17 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
             const v8i aop = as_v8i(alo[i & 1], ahi[i & 1]);
 #pragma unroll
             for (int j = 0; j < WN; ++j)
-              acc[i][j] = mfma_wt<AF, S, S>(bop[j], aop, acc[i][j], (int)sx[j], axr[i & 1]);
+              acc[i][j] = mfma_wt<AF, S, MXA ? S : 0>(bop[j], aop, acc[i][j], (int)sx[j],
+                                                     MXA ? axr[i & 1] : 127);
           }
           __builtin_amdgcn_sched_barrier(0);
           issue_part(i);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
-        // per-token E4M3 GEMM1 and E2M1 (W4A4) activations: the compiler's own
-        // order (all of the step's fragments read before the first MFMA)
-        // measured 2-3 % faster than the order above
+        // E2M1 (W4A4) activations: the compiler's own order (all of the
+        // step's fragments read before the first MFMA) measured 2-3 % faster
+        // than the order above
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
           const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
