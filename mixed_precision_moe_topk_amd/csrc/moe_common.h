@@ -75,9 +75,6 @@ typedef short v2s __attribute__((ext_vector_type(2)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- numerics
-// Round a finite float to the nearest OCP E4M3 ("FN") code: ties to even
-// mantissa, magnitudes above 448 saturate to 448, the sign is kept when the
-// magnitude rounds to zero.  Integer bit manipulation on the float32 pattern.
 // Nearest E2M1 magnitude code (0, 0.5, 1, 1.5, 2, 3, 4, 6 -> 0..7) of a
 // non-negative value, ties to the even code, saturating at 6.
 __device__ __forceinline__ uint32_t e2m1_magnitude_code(float v_abs) {
@@ -105,19 +102,30 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   return min(max(fl - EMAX, -127), 127);
 }
 
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fminf(fabsf(v), 448.0f);
-  uint32_t code;
-  if (a < 0.015625f) {
-    // below the smallest normal 2^-6 the codes are multiples of 2^-9; 8 is 0x08
-    code = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    uint32_t b = __float_as_uint(a);
-    b += 0x7FFFFu + ((b >> 20) & 1u);  // round to 3 mantissa bits, ties to even
-    code = (b >> 20) - (120u << 3);    // exponent bias 127 -> 7
-  }
-  return sign | code;
+// E4M3 codes of two floats of magnitude at most 448, as bytes 0 and 1:
+// gfx950's v_cvt_pk_fp8_f32 (OCP E4M3 "FN": bias 7, round to nearest even,
+// sign kept when the magnitude rounds to zero, 2^-9-spaced codes below 2^-6).
+// On the device it gave the same code as a bit-manipulation encoder of that
+// definition for every float32 of magnitude <= 464, of either sign; callers
+// clamp larger magnitudes to 448 first (saturation).
+__device__ __forceinline__ uint32_t e4m3_pk(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// fl32(v / s) as far as its E4M3 code goes, with inv = fl32(1 / s): the
+// product v * inv is within 2 ulp of the IEEE quotient fl32(v / s) (each of
+// the two roundings contributes at most 2^-24 relative error), so both lie on
+// the same side of every E4M3 rounding midpoint, and encode alike, unless
+// the product is within 2 ulp of a midpoint (the 20 bits below the E4M3
+// mantissa equal 0x80000 +- 2) or below 2^-6, where the E4M3 grid is
+// uniform and midpoints sit at other bit positions; those rare values take
+// the exact quotient, as do non-finite products (a tiny s whose reciprocal
+// overflows).  Saves the ~10-instruction IEEE division per element.
+__device__ __forceinline__ float div_for_e4m3(float v, float s, float inv) {
+  const float q = v * inv;
+  const uint32_t a = __float_as_uint(q) & 0x7FFFFFFFu;
+  const bool exact = a < 0x3C800000u || a >= 0x7F800000u || ((a & 0xFFFFFu) - 0x7FFFEu) <= 4u;
+  return exact ? __fdiv_rn(v, s) : q;
 }
 
 // float32 -> bf16 bits, round to nearest even (finite inputs).

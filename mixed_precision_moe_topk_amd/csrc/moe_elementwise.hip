@@ -35,14 +35,16 @@ __device__ __forceinline__ float bf16x8_amax(const uint4& u, float amax) {
   return amax;
 }
 
-__device__ __forceinline__ uint2 bf16x8_to_e4m3(const uint4& u, float s) {
+// E4M3 codes of fl32(x / s) for eight bf16 values (|x| <= amax, so the
+// quotients stay within 448 * (1 + 2^-23)); inv = fl32(1 / s).
+__device__ __forceinline__ uint2 bf16x8_to_e4m3(const uint4& u, float s, float inv) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
   uint32_t c[2] = {0, 0};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t lo = e4m3_encode(__fdiv_rn(__uint_as_float(w[j] << 16), s));
-    const uint32_t hi = e4m3_encode(__fdiv_rn(__uint_as_float(w[j] & 0xFFFF0000u), s));
-    c[j / 2] |= (lo | (hi << 8)) << (16 * (j & 1));
+    const float lo = div_for_e4m3(__uint_as_float(w[j] << 16), s, inv);
+    const float hi = div_for_e4m3(__uint_as_float(w[j] & 0xFFFF0000u), s, inv);
+    c[j / 2] |= e4m3_pk(lo, hi) << (16 * (j & 1));
   }
   return make_uint2(c[0], c[1]);
 }
@@ -71,10 +73,11 @@ __global__ __launch_bounds__(256) void k_quant_tokens(const uint16_t* __restrict
     for (int r = 0; r < kR; ++r) amax = bf16x8_amax(u[r], amax);
     amax = block_max256(amax, red);
     const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    const float inv = __fdiv_rn(1.0f, s);
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
       const int i = threadIdx.x + 256 * r;
-      if (i < nv) out[i] = bf16x8_to_e4m3(u[r], s);
+      if (i < nv) out[i] = bf16x8_to_e4m3(u[r], s, inv);
     }
     if (threadIdx.x == 0) scales[t] = s;
     return;
@@ -82,7 +85,8 @@ __global__ __launch_bounds__(256) void k_quant_tokens(const uint16_t* __restrict
   for (int i = threadIdx.x; i < nv; i += blockDim.x) amax = bf16x8_amax(row[i], amax);
   amax = block_max256(amax, red);
   const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-  for (int i = threadIdx.x; i < nv; i += blockDim.x) out[i] = bf16x8_to_e4m3(row[i], s);
+  const float inv = __fdiv_rn(1.0f, s);
+  for (int i = threadIdx.x; i < nv; i += blockDim.x) out[i] = bf16x8_to_e4m3(row[i], s, inv);
   if (threadIdx.x == 0) scales[t] = s;
 }
 
@@ -110,9 +114,9 @@ __global__ __launch_bounds__(256) void k_requant(const float* __restrict__ h, in
   auto f4_amax = [](const float4& v, float a) {
     return fmaxf(fmaxf(a, fabsf(v.x)), fmaxf(fabsf(v.y), fmaxf(fabsf(v.z), fabsf(v.w))));
   };
-  auto f4_e4m3 = [](const float4& v, float s) {
-    return e4m3_encode(__fdiv_rn(v.x, s)) | (e4m3_encode(__fdiv_rn(v.y, s)) << 8) |
-           (e4m3_encode(__fdiv_rn(v.z, s)) << 16) | (e4m3_encode(__fdiv_rn(v.w, s)) << 24);
+  auto f4_e4m3 = [](const float4& v, float s, float inv) {
+    return e4m3_pk(div_for_e4m3(v.x, s, inv), div_for_e4m3(v.y, s, inv)) |
+           (e4m3_pk(div_for_e4m3(v.z, s, inv), div_for_e4m3(v.w, s, inv)) << 16);
   };
   uint32_t* out = reinterpret_cast<uint32_t*>(codes + r * I);
   float amax = 0.0f;
@@ -128,10 +132,11 @@ __global__ __launch_bounds__(256) void k_requant(const float* __restrict__ h, in
     for (int q = 0; q < kR; ++q) amax = f4_amax(v[q], amax);
     amax = block_max256(amax, red);
     const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    const float inv = __fdiv_rn(1.0f, s);
 #pragma unroll
     for (int q = 0; q < kR; ++q) {
       const int i = threadIdx.x + 256 * q;
-      if (i < nv) out[i] = f4_e4m3(v[q], s);
+      if (i < nv) out[i] = f4_e4m3(v[q], s, inv);
     }
     if (threadIdx.x == 0) scales[r] = s;
     return;
@@ -139,7 +144,8 @@ __global__ __launch_bounds__(256) void k_requant(const float* __restrict__ h, in
   for (int i = threadIdx.x; i < nv; i += blockDim.x) amax = f4_amax(row[i], amax);
   amax = block_max256(amax, red);
   const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-  for (int i = threadIdx.x; i < nv; i += blockDim.x) out[i] = f4_e4m3(row[i], s);
+  const float inv = __fdiv_rn(1.0f, s);
+  for (int i = threadIdx.x; i < nv; i += blockDim.x) out[i] = f4_e4m3(row[i], s, inv);
   if (threadIdx.x == 0) scales[r] = s;
 }
 
@@ -175,8 +181,12 @@ __device__ __forceinline__ uint2 mx_quant8(const float (&v)[8], bool valid, uint
     if (E2M1)
       c[0] |= (e2m1_magnitude_code(fabsf(v[i]) * inv) | ((__float_as_uint(v[i]) >> 31) << 3))
               << (4 * i);
-    else
-      c[i / 4] |= e4m3_encode(v[i] * inv) << (8 * (i & 3));
+  }
+  if (!E2M1) {  // v * 2^-X is below 512 in magnitude; saturate at 448 as the encoder does
+#pragma unroll
+    for (int i = 0; i < 8; i += 2)
+      c[i / 4] |= e4m3_pk(fminf(fmaxf(v[i] * inv, -448.0f), 448.0f),
+                          fminf(fmaxf(v[i + 1] * inv, -448.0f), 448.0f)) << (8 * (i & 3));
   }
   return make_uint2(c[0], c[1]);
 }

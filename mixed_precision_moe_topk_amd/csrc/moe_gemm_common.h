@@ -335,12 +335,15 @@ __device__ __forceinline__ void epilogue_fc1_mx_t(const GemmParams& p, const v4f
           *reinterpret_cast<uint16_t*>(qrow + 16 * b + 8 + 2 * g4) = (uint16_t)n1;
         }
       } else if (live) {
-        uint32_t w0 = 0, w1 = 0;
+        // x * 2^-X is below 512 in magnitude; saturate at 448 as the encoder does
+        float y0[4], y1[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          w0 |= e4m3_encode(x0[v] * inv) << (8 * v);
-          w1 |= e4m3_encode(x1[v] * inv) << (8 * v);
+          y0[v] = fminf(fmaxf(x0[v] * inv, -448.0f), 448.0f);
+          y1[v] = fminf(fmaxf(x1[v] * inv, -448.0f), 448.0f);
         }
+        const uint32_t w0 = e4m3_pk(y0[0], y0[1]) | (e4m3_pk(y0[2], y0[3]) << 16);
+        const uint32_t w1 = e4m3_pk(y1[0], y1[1]) | (e4m3_pk(y1[2], y1[3]) << 16);
         *reinterpret_cast<uint32_t*>(qrow + 32 * b + 4 * g4) = w0;
         *reinterpret_cast<uint32_t*>(qrow + 32 * b + 16 + 4 * g4) = w1;
       }

@@ -171,6 +171,43 @@ def test_quantize_tokens_matches_oracle(afmt, T, H, seed):
     assert np.all(gs == 1.0)
 
 
+@pytest.mark.parametrize("afmt", ["fp8", "mxfp8", "mxfp4"])
+def test_quantize_tokens_tiny_and_huge_rows(afmt):
+    """Token rows scaled by 2^-100 ... 2^-131 (amax / 448 subnormal, 1 / s
+    beyond the float32 range, bf16 subnormal elements) and by 2^100, rounded
+    to bf16: codes and scales bit-exact against the oracle's quantiser."""
+    import torch
+
+    import mixed_precision_moe_topk_amd as M
+
+    H = 512
+    exps = [-100, -115, -119, -120, -122, -124, -126, -128, -131, 100, 0]
+    x0 = F.bf16_to_f32(MI.hidden_bf16(211, len(exps), H))
+    x = np.stack([x0[i] * np.float32(2.0 ** e) for i, e in enumerate(exps)]).astype(np.float32)
+    bits = F.bf16_rne(x)
+    x = F.bf16_to_f32(bits)
+    T = len(exps)
+    d = M.LayerDims(8, H, 256, "mxfp4", afmt)
+    cols = H // 2 if afmt == "mxfp4" else H
+    codes = torch.empty((T, cols), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(T, dtype=torch.float32, device="cuda")
+    mx = afmt != "fp8"
+    bsc = torch.empty((T, mx_scale_row_bytes(H)), dtype=torch.uint8, device="cuda") if mx else None
+    M.quantize_tokens(d, torch.from_numpy(bits.view(np.int16)).cuda(), codes, scales, bsc)
+    torch.cuda.synchronize()
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    if afmt == "fp8":
+        rc, rs = Q.e4m3_rows(x)
+        assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32)), (gs, rs)
+        for t in range(T):
+            assert np.array_equal(gc[t], rc[t]), (exps[t], np.count_nonzero(gc[t] != rc[t]))
+        return
+    rc, rsc = Q.mxfp8_rows(x) if afmt == "mxfp8" else Q.mxfp4_quantize(x)
+    for t in range(T):
+        assert np.array_equal(gc[t], rc[t]), exps[t]
+    assert np.array_equal(mx_scales_canonical(bsc.cpu().numpy(), H), rsc)
+
+
 def test_quantize_tokens_bf16_unsupported():
     import torch
 
