@@ -591,11 +591,6 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   constexpr int WN = kWN;
   using L = Map<WM, MXA, A4>;
   constexpr int NF = L::kNF;
-  // GEMM2 with E4M3 or MXFP8 inputs: the step order pipelined across the
-  // barrier (same-box A/B against the orders below: MXFP8 4096-token GEMM2
-  // 13 % faster, E4M3 3 % / 5 % on the 4096 / 16384-token DeepSeek GEMM2;
-  // on GEMM1 it was 2-4 % slower)
-  constexpr bool PIPE = !A4 && !FC1;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = lane_id();
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   // Wave row wm owns the tile's 16-row groups 2i + wm (i < WM), so a partly
@@ -697,7 +692,6 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
     for (int i = 0; i < WM; ++i) sc[i] = 1.0f;
   }
   uint32_t sx[WN];
-  uint4 bq[WN];          // weight fragments (the E2M1 operand is built at each MFMA)
   uint4 alo[2], ahi[2];  // A fragment halves, two subtiles in flight
   int axr[2];            // MXFP8: the A scale dwords of those subtiles
 
@@ -720,7 +714,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   auto read_a = [&](const uint8_t* as, const uint8_t* sa, int i, int buf)
                     __attribute__((always_inline)) {
     alo[buf] = *reinterpret_cast<const uint4*>(as + i * kSub);
-    ahi[buf] = *reinterpret_cast<const uint4*>(as + i * kSub + 1024);
+    if constexpr (!A4) ahi[buf] = *reinterpret_cast<const uint4*>(as + i * kSub + 1024);
     if constexpr (MXA) axr[buf] = *reinterpret_cast<const int*>(sa + i * kSaSub);
   };
 
@@ -747,137 +741,84 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
         if constexpr (S == 0) issue_sx(min((ks >> 2) + 1, KS4 - 1), ((ks >> 2) + 1) & 1);
       }
     };
-    if constexpr (PIPE) {
-      // GEMM2 (E4M3 / MXFP8 inputs), software-pipelined across the barrier:
-      // the step enters with its weight fragments, scale words and the A
-      // fragment of subtile 0 already in registers; subtile i + 1 is read
-      // while the MFMAs of subtile i run; the barrier that publishes the next
-      // step's tiles sits before the last subtile, whose MFMAs then each
-      // give way to the read of one of the next step's weight fragments.
-      // Placed after the last subtile, the barrier left each SIMD's matrix
-      // pipe idle until the eight waves' fragment reads had all come back.
-      constexpr int P0 = (S * WM) & 1;  // A register buffer of subtile 0
-      const uint8_t* as = a_at(S & 1);
-      const uint8_t* sa = sa_at(ks);
+    // all of the step's weight fragments are read after the barrier that
+    // ends the previous step
+    const uint8_t* bs = b_at(bstage);
+    if constexpr (S == 0) {
+      const uint8_t* ss = sx_at(ks);
 #pragma unroll
-      for (int i = 0; i + 1 < WM; ++i) {
-        read_a(as, sa, i + 1, (P0 + i + 1) & 1);
-        if (cols && i < nvalid) {
-          const v8i aop = as_v8i(alo[(P0 + i) & 1], ahi[(P0 + i) & 1]);
-          const int ax = MXA ? axr[(P0 + i) & 1] : 127;
-#pragma unroll
-          for (int j = 0; j < WN; ++j)
-            acc[i][j] = mfma_wt<AF, S, MXA ? S : 0>(fp4_operand(bq[j]), aop, acc[i][j],
-                                                   (int)sx[j], ax);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (i < 4) issue_part(i);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int part = WM - 1; part < 4; ++part) issue_part(part);
-      wait_barrier<(S == 0 ? 2 * kBPW : kBPW)>();
-      // The reads below take the next step's tiles (past the last step they
-      // read LDS whose contents are never used).
-      constexpr int IL = WM - 1;
-      const uint8_t* bn = b_at(bstage == 2 ? 0 : bstage + 1);
-      const uint8_t* sn = sx_at(ks + 1);
-      const v8i aop = as_v8i(alo[(P0 + IL) & 1], ahi[(P0 + IL) & 1]);
-      const int ax = MXA ? axr[(P0 + IL) & 1] : 127;
-      const bool last = cols && IL < nvalid;
+      for (int j = 0; j < WN; ++j) sx[j] = *reinterpret_cast<const uint32_t*>(ss + j * 256);
+    }
+    const uint8_t* sa = sa_at(ks);
+    const uint8_t* as = a_at(S & 1);
+    v8i bop[WN];
+    if constexpr (!A4) {
+      // E4M3 codes (per-token or MXFP8), both GEMMs: LDS reads in MFMA
+      // order, the A fragment (and MXFP8 scale) of subtile 0 and the weight
+      // fragments first, then those of subtile i + 1 while the MFMAs of
+      // subtile i run, so a subtile's MFMAs do not wait for its own reads.
+      // Only two A fragments are live at a time (the MXFP8 activation
+      // scales fit in the 160-row tile).  The reads are unconditional
+      // (subtiles past the tile end hold copies of its last row); only the
+      // MFMAs of such subtiles are skipped.  For per-token E4M3 this order
+      // was 2-4 % slower than the compiler's own while the row-per-register
+      // epilogue's scales took 20 registers; with transposed accumulators
+      // (5 scales) it is faster on both GEMMs (same box, DeepSeek-V4-Pro
+      // GEMM1 3.38 -> 3.29 ms; GEMM2 2.198 -> 2.113 ms against an order that
+      // moved the barrier before the last subtile and read the next step's
+      // weight fragments between its MFMAs, which is also 2-3 % slower on
+      // the MXFP8 GEMM2 now and was removed).
+      read_a(as, sa, 0, 0);
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
-        if (last)
-          acc[IL][j] = mfma_wt<AF, S, MXA ? S : 0>(fp4_operand(bq[j]), aop, acc[IL][j],
-                                                  (int)sx[j], ax);
-        bq[j] = *reinterpret_cast<const uint4*>(bn + j * 1024);
-        if constexpr (S == 3) sx[j] = *reinterpret_cast<const uint32_t*>(sn + j * 256);
+        const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
+        bop[j] = fp4_operand(b);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        if (i + 1 < WM) read_a(as, sa, i + 1, (i + 1) & 1);
+        if (cols && i < nvalid) {
+          const v8i aop = as_v8i(alo[i & 1], ahi[i & 1]);
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            acc[i][j] = mfma_wt<AF, S, MXA ? S : 0>(bop[j], aop, acc[i][j], (int)sx[j],
+                                                   MXA ? axr[i & 1] : 127);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue_part(i);
         __builtin_amdgcn_sched_barrier(0);
       }
-      read_a(a_at((S + 1) & 1), sa_at(ks + 1), 0, (P0 + WM) & 1);
     } else {
-      // all of the step's weight fragments are read after the barrier that
-      // ends the previous step
-      const uint8_t* bs = b_at(bstage);
-      if constexpr (S == 0) {
-        const uint8_t* ss = sx_at(ks);
+      // E2M1 (W4A4) activations: the compiler's own order (all of the
+      // step's fragments read before the first MFMA); the order above
+      // measured 2-3 % slower here, and equal since the transposed
+      // accumulators
 #pragma unroll
-        for (int j = 0; j < WN; ++j) sx[j] = *reinterpret_cast<const uint32_t*>(ss + j * 256);
+      for (int j = 0; j < WN; ++j) {
+        const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
+        bop[j] = fp4_operand(b);
       }
-      const uint8_t* sa = sa_at(ks);
-      const uint8_t* as = a_at(S & 1);
-      v8i bop[WN];
-      if constexpr (!A4) {
-        // GEMM1 with E4M3 codes (per-token or MXFP8): LDS reads in MFMA
-        // order, the A fragment (and MXFP8 scale) of subtile 0 and the weight
-        // fragments first, then those of subtile i + 1 while the MFMAs of
-        // subtile i run, so a subtile's MFMAs do not wait for its own reads.
-        // Only two A fragments are live at a time (the MXFP8 activation
-        // scales fit in the 160-row tile).  The reads are unconditional
-        // (subtiles past the tile end hold copies of its last row); only the
-        // MFMAs of such subtiles are skipped.  For per-token E4M3 this order
-        // was 2-4 % slower than the compiler's own while the row-per-register
-        // epilogue's scales took 20 registers; with transposed accumulators
-        // (5 scales) it is 2.8 % faster on the 16384-token DeepSeek-V4-Pro
-        // GEMM1 (3.38 -> 3.29 ms, same box).
-        read_a(as, sa, 0, 0);
 #pragma unroll
-        for (int j = 0; j < WN; ++j) {
-          const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
-          bop[j] = fp4_operand(b);
+      for (int i = 0; i < WM; ++i) {
+        if (cols && i < nvalid) {
+          const v8i aop = fp4_operand(*reinterpret_cast<const uint4*>(as + i * kSub));
+          const int ax = *reinterpret_cast<const int*>(sa + i * kSaSub);
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            acc[i][j] = mfma_wt<AF, S, MXA ? S : 0>(bop[j], aop, acc[i][j], (int)sx[j], ax);
         }
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < WM; ++i) {
-          if (i + 1 < WM) read_a(as, sa, i + 1, (i + 1) & 1);
-          if (cols && i < nvalid) {
-            const v8i aop = as_v8i(alo[i & 1], ahi[i & 1]);
-#pragma unroll
-            for (int j = 0; j < WN; ++j)
-              acc[i][j] = mfma_wt<AF, S, MXA ? S : 0>(bop[j], aop, acc[i][j], (int)sx[j],
-                                                     MXA ? axr[i & 1] : 127);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          issue_part(i);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-        // E2M1 (W4A4) activations: the compiler's own order (all of the
-        // step's fragments read before the first MFMA) measured 2-3 % faster
-        // than the order above
-#pragma unroll
-        for (int j = 0; j < WN; ++j) {
-          const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
-          bop[j] = fp4_operand(b);
-        }
-#pragma unroll
-        for (int i = 0; i < WM; ++i) {
-          if (cols && i < nvalid) {
-            const uint4 lo = *reinterpret_cast<const uint4*>(as + i * kSub);
-            v8i aop;
-            if constexpr (A4) {
-              aop = fp4_operand(lo);
-            } else {
-              const uint4 hi = *reinterpret_cast<const uint4*>(as + i * kSub + 1024);
-              aop = as_v8i(lo, hi);
-            }
-            const int ax = MXA ? *reinterpret_cast<const int*>(sa + i * kSaSub) : 127;
-#pragma unroll
-            for (int j = 0; j < WN; ++j)
-              acc[i][j] = mfma_wt<AF, S, MXA ? S : 0>(bop[j], aop, acc[i][j], (int)sx[j], ax);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          issue_part(i);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        issue_part(i);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // subtiles fewer than the four load parts
-#pragma unroll
-      for (int part = WM; part < 4; ++part) issue_part(part);
-      // the loads of step ks+1 (A issued above, weights one step earlier) have
-      // landed once only the loads issued after this step's A loads remain
-      wait_barrier<(S == 0 ? 2 * kBPW : kBPW)>();
     }
+    // subtiles fewer than the four load parts
+#pragma unroll
+    for (int part = WM; part < 4; ++part) issue_part(part);
+    // the loads of step ks+1 (A issued above, weights one step earlier) have
+    // landed once only the loads issued after this step's A loads remain
+    wait_barrier<(S == 0 ? 2 * kBPW : kBPW)>();
   };
 
   // prologue: A and weights (and scales) of step 0, weights of step 1
@@ -887,16 +828,6 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   issue_sx(0, 0);
   issue_b(min(1, KS - 1), 1);
   wait_barrier<kBPW>();
-  if constexpr (PIPE) {
-    const uint8_t* b0 = b_at(0);
-    const uint8_t* s0 = sx_at(0);
-#pragma unroll
-    for (int j = 0; j < WN; ++j) {
-      bq[j] = *reinterpret_cast<const uint4*>(b0 + j * 1024);
-      sx[j] = *reinterpret_cast<const uint32_t*>(s0 + j * 256);
-    }
-    read_a(a_at(0), sa_at(0), 0, 0);
-  }
   int ks = 0, bstage = 0;
   for (; ks + 4 <= KS; ks += 4) {
     step(std::integral_constant<int, 0>{}, ks, bstage);
