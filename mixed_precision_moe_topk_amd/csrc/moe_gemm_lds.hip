@@ -5,10 +5,6 @@
 // each 128-wide K step.
 #include "moe_gemm_common.h"
 
-#ifndef MOE_INTERLEAVE
-#define MOE_INTERLEAVE 1
-#endif
-
 namespace moe {
 
 // Scheduling hint for one K step: NMFMA MFMAs with NVMEM global loads and NDS
@@ -213,11 +209,6 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
     load_b(min(ks + PB, KS - 1), bq[(S + PB) % NB]);
     constexpr bool LOAD_SX = (S + PB) % 4 == 0;
     if constexpr (LOAD_SX) load_sx(min(ks + PB, KS - 1), sx_next);
-#if !MOE_INTERLEAVE
-    // keep the step's phases in order (prefetch | LDS reads + MFMAs | LDS
-    // writes + barrier) so the wait counts refer to the intended loads
-    __builtin_amdgcn_sched_barrier(0);
-#endif
     const uint8_t* abuf = lds + (S & 1) * ABUF + (WM * wm) * (NF * 1024);
     v8i bop[WN];
     float gs[WN];  // INT4: this step's group scale of the lane's column
@@ -252,11 +243,9 @@ __device__ __forceinline__ void gemm_lds_body(const GemmParams& p, uint8_t* lds,
         }
       }
     }
-#if MOE_INTERLEAVE
     // issue order inside the step: the wave's global loads and LDS reads are
     // spread between its MFMAs so they issue while the matrix pipe is busy
     if (FULL) interleave_schedule<WM * WN, (LOAD_SX ? 2 : 1) * WN + NCH + (LOAD_SX && MXA ? WM : 0), NF * WM>();
-#endif
     __builtin_amdgcn_sched_barrier(0);
     // A of step ks+1 (a harmless copy of the last step once past the end)
     store_a((S + 1) & 1, ast[(S + 1) % AS]);
