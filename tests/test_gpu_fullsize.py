@@ -6,7 +6,8 @@ oracle's quantiser of the GPU's h (bit-exact); SwiGLU and GEMM2 output of
 chosen rows (every row of the last, partial M-tile and of the second 16-row
 group of the first tile, for the hottest, the coldest and random experts:
 the tile tails and the second wave row), against the oracle's pass of that
-one expert; and the bf16 layer output for random tokens, computed token by
+one expert; the whole h and y2 rows of the last row of every active expert
+(every expert's last M-tile, every N-tile of both GEMMs); and the bf16 layer output for random tokens, computed token by
 token by the oracle (the layer is independent per token), within the output
 contract.
 
@@ -17,6 +18,7 @@ import pytest
 import moe_inputs as MI
 import oracle as O
 from oracle import formats as F
+from tests import oracle_rows as OR
 from tests.harness import Problem, check_output, expected_work_map, rel_l2
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -151,6 +153,26 @@ def test_fullsize_sampled(name):
             assert rel_l2(g["h"][grow], sub["h"][orow]) <= 1e-4, e
         assert rel_l2(g["y2"][grow], sub["y2"][orow]) <= 2e-3, e
         print(f"{name}: expert {e} ({r1 - r0} rows, tile_m {tm}): {len(grow)} tail rows checked")
+    # the last row of every active expert (a row of its last, partial M-tile),
+    # whole h and y2 rows, so every GEMM1 and GEMM2 N-tile of every expert has
+    # a checked row; the oracle's expert passes run in worker processes
+    last_rows = [int(off[e + 1]) - 1 for e in p.active]
+    jobs = [(name, e, p.hidden[[tok[r]]], p.logits[[tok[r]]]) for e, r in zip(p.active, last_rows)]
+    got_h, got_y2, ref_h, ref_y2 = [], [], [], []
+    for (e, h_ref, y2_ref), r in zip(OR.expert_rows_many(jobs), last_rows):
+        got_y2.append(g["y2"][r])
+        ref_y2.append(y2_ref[0])
+        # a wrong row or tile is off by O(1); the bound leaves room for an
+        # FC2 code that flipped on h's float32 rounding
+        assert rel_l2(g["y2"][r], y2_ref[0]) <= 2e-2, (e, r)
+        if g["h"] is not None:
+            got_h.append(g["h"][r])
+            ref_h.append(h_ref[0])
+            assert rel_l2(g["h"][r], h_ref[0]) <= 1e-4, (e, r)
+    assert rel_l2(np.stack(got_y2), np.stack(ref_y2)) <= 2e-3
+    if got_h:
+        assert rel_l2(np.stack(got_h), np.stack(ref_h)) <= 1e-4
+    print(f"{name}: last rows of all {len(p.active)} active experts checked")
     # sampled tokens end to end
     r = p.run_oracle(tokens=sample)
     rows = g["slot_row"][sample].reshape(-1)
