@@ -507,8 +507,13 @@ __global__ __launch_bounds__(kWave * NW, MINB) void k_gemm_ab(GemmParams p) {
 // Operands reach LDS by global_load_lds (16 bytes per lane, lane L of a wave
 // instruction lands at M0 + 16 L; an SALU write of M0 needs one wait state
 // before the load reads it), so no staging registers are needed:
-//   A       2 stages x 20 KB  fragment (g, h) of 16-row group g at (2g+h) KB,
-//                             lane L's 16-byte operand piece at 16 L
+//   A       2 stages x 20 KB  16-row group g at 2g KB: E4M3 rows 0-7 in its
+//                             first KB, rows 8-15 in the second, each KB
+//                             8 rows x 128 bytes chunk-major (chunk c of
+//                             row r at 16 (8c + r)), so one load moves
+//                             whole 128-byte lines; E2M1 (64 bytes per row
+//                             and step): 1 KB per group, lane L's piece at
+//                             16 L
 //   weights 3 stages x 32 KB  16-column block b at b KB, in device order
 //   scales  2 slots x 8 KB (one 4-step group of E8M0 words each), block b
 //           at 256 b
@@ -608,12 +613,22 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   // (waves below L::kRG - 8) g = wave + 8: row 16 g + L%16 of the tile (the
   // last row repeated past the end), operand piece L/16
   const bool two_rg = wave < L::kRG - kNW;  // compile-time false when L::kRG == kNW
-  const int kofs = 16 * (lane >> 4);
-  const int ar0 = min(tile.row0 + 16 * wave + (lane & 15), row_end - 1);
-  const int ar1 = min(tile.row0 + 16 * (wave + kNW) + (lane & 15), row_end - 1);
-  const uint8_t* arow0 = p.a + (FC1 ? (int64_t)p.row_token[ar0] : (int64_t)ar0) * p.a_stride + kofs;
-  const uint8_t* arow1 = p.a + (FC1 ? (int64_t)p.row_token[ar1] : (int64_t)ar1) * p.a_stride + kofs;
-  constexpr int kAHalf = 64;  // k offset of the second operand half
+  // E4M3 A: one load covers 8 rows x 128 bytes (lane L: row L % 8, 16-byte
+  // chunk L / 8), two loads a 16-row group, so each load fetches whole
+  // 128-byte lines (with 16 rows x 64 bytes, the layout the MFMA lanes read,
+  // every load touched 16 half lines: same-box, DeepSeek-V4-Pro GEMM2
+  // 2.115 -> 2.085 ms, DeepSeek-V3 prefill GEMM1 0.865 -> 0.855 ms);
+  // E2M1 A: 16 rows x 64 bytes
+  const int kofs = A4 ? 16 * (lane >> 4) : 16 * (lane >> 3);
+  const int rl = A4 ? (lane & 15) : (lane & 7);
+  auto arow = [&](int r) __attribute__((always_inline)) {
+    const int rr = min(r, row_end - 1);
+    return p.a + (FC1 ? (int64_t)p.row_token[rr] : (int64_t)rr) * p.a_stride + kofs;
+  };
+  const uint8_t* arow0 = arow(tile.row0 + 16 * wave + rl);
+  const uint8_t* arow1 = arow(tile.row0 + 16 * (wave + kNW) + rl);
+  const uint8_t* arow0h = A4 ? arow0 : arow(tile.row0 + 16 * wave + 8 + rl);
+  const uint8_t* arow1h = A4 ? arow1 : arow(tile.row0 + 16 * (wave + kNW) + 8 + rl);
   // weights: this wave loads 16-column blocks kBPW wave + u (clamped to N)
   const uint8_t* wcol[kBPW];
 #pragma unroll
@@ -626,10 +641,10 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
       if (two_rg) lds_dma16(arow1 + ks * (kKStep / 2), dst + kNW * 1024);
     } else {
       lds_dma16(arow0 + ks * kKStep, dst);
-      lds_dma16(arow0 + ks * kKStep + kAHalf, dst + 1024);
+      lds_dma16(arow0h + ks * kKStep, dst + 1024);
       if (two_rg) {
         lds_dma16(arow1 + ks * kKStep, dst + kNW * 2048);
-        lds_dma16(arow1 + ks * kKStep + kAHalf, dst + kNW * 2048 + 1024);
+        lds_dma16(arow1h + ks * kKStep, dst + kNW * 2048 + 1024);
       }
     }
   };
@@ -689,8 +704,12 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   auto b_at = [&](int bst) __attribute__((always_inline)) {
     return lds + L::kBOff + bst * kBBuf + (wn * WN) * 1024 + lane * 16;
   };
+  // MFMA lane (r, g) = (lane % 16, lane / 16): its low operand piece (k =
+  // 16 g + [0, 16)) is chunk g of row r, at byte ((r / 8) * 64 + 8 g + r % 8) * 16
+  // of the group; the high piece (k = 64 + 16 g + [0, 16)) 512 bytes later
+  const int aoff = A4 ? lane * 16 : (((lane >> 3) & 1) * 64 + 8 * (lane >> 4) + (lane & 7)) * 16;
   auto a_at = [&](int ast) __attribute__((always_inline)) {
-    return lds + L::kAOff + ast * L::kABuf + wm * (NF * 1024) + lane * 16;
+    return lds + L::kAOff + ast * L::kABuf + wm * (NF * 1024) + aoff;
   };
   auto sx_at = [&](int ksx) __attribute__((always_inline)) {
     return lds + L::kSOff + ((ksx >> 2) & 1) * kSxSlot + (wn * WN) * 256 + lane * 4;
@@ -703,7 +722,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   auto read_a = [&](const uint8_t* as, const uint8_t* sa, int i, int buf)
                     __attribute__((always_inline)) {
     alo[buf] = *reinterpret_cast<const uint4*>(as + i * kSub);
-    if constexpr (!A4) ahi[buf] = *reinterpret_cast<const uint4*>(as + i * kSub + 1024);
+    if constexpr (!A4) ahi[buf] = *reinterpret_cast<const uint4*>(as + i * kSub + 512);
     if constexpr (MXA) axr[buf] = *reinterpret_cast<const int*>(sa + i * kSaSub);
   };
 
