@@ -37,12 +37,19 @@ SMALL = [
     # remainder of 2 or 3 steps) in both GEMMs
     (300, 5, 2, 768, 896, "mxfp4", "mxfp8", 36, 1.0),
     (300, 5, 2, 896, 768, "mxfp4", "fp8", 37, 0.0),
+    # several 160-row M-tiles per expert and several 512-column N-tiles in
+    # both GEMMs (N tails of 256 columns in GEMM2 for H = 1280)
+    (900, 6, 2, 1536, 512, "mxfp4", "fp8", 38, 0.0),
+    (1500, 3, 2, 2048, 1536, "mxfp4", "fp8", 39, 0.0),
+    (700, 5, 2, 1280, 1024, "mxfp4", "mxfp8", 40, 0.0),
+    (600, 8, 2, 1536, 512, "int4", "fp8", 41, 0.0),
     # W4A4 (MXFP4 activations): every tile configuration, partial scale groups
     (70, 6, 3, 384, 256, "mxfp4", "mxfp4", 51, 0.0),  # 64-row tiles
     (300, 5, 2, 256, 384, "mxfp4", "mxfp4", 52, 2.0), # 160-row tiles, tails
     (400, 4, 2, 384, 640, "mxfp4", "mxfp4", 53, 1.0), # full + ragged 160-row tiles, N tail
     (9, 40, 4, 512, 128, "mxfp4", "mxfp4", 54, 0.0),  # 16-row tiles, empty experts
     (6, 1, 1, 8320, 4224, "mxfp4", "mxfp4", 55, 0.0), # long rows
+    (900, 6, 2, 1536, 512, "mxfp4", "mxfp4", 56, 0.0), # several M- and N-tiles
 ]
 
 
