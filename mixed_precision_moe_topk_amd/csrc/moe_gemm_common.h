@@ -266,13 +266,14 @@ __device__ __forceinline__ void store4(float* dst, float x, float y, float z, fl
 template <bool FC1, int WM, int WN, int RS = 16>
 __device__ __forceinline__ void epilogue_t(const GemmParams& p, const v4f (&acc)[WM][WN],
                                            const float (&sc)[WM], int row_base, int row_end,
-                                           int nvalid, int64_t nb0, int jvalid, int lane) {
+                                           int nvalid, int64_t nb0, int jvalid, int lane,
+                                           int i0 = 0, int i1 = WM) {
   const int c4 = 4 * (lane >> 4);
   if constexpr (FC1 && WN % 4 == 0) {
     const bool lo = (lane & 8) == 0;
     const int rr = lane & 7;
 #pragma unroll
-    for (int i = 0; i < WM; ++i) {
+    for (int i = 0; i < WM; ++i) { if (i < i0 || i >= i1) continue;
       if (i >= nvalid) continue;
       const float s = sc[i];
       const int r0 = row_base + RS * i;
@@ -301,7 +302,7 @@ __device__ __forceinline__ void epilogue_t(const GemmParams& p, const v4f (&acc)
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < WM; ++i) {
+    for (int i = 0; i < WM; ++i) { if (i < i0 || i >= i1) continue;
       if (i >= nvalid) continue;
       const int r = row_base + RS * i + (lane & 15);
       if (r >= row_end) continue;
@@ -336,12 +337,13 @@ __device__ __forceinline__ void epilogue_t(const GemmParams& p, const v4f (&acc)
 template <bool E2M1, int WM, int WN, int RS = 16>
 __device__ __forceinline__ void epilogue_fc1_mx_t(const GemmParams& p, const v4f (&acc)[WM][WN],
                                                   int row_base, int row_end, int nvalid,
-                                                  int64_t nb0, int jvalid, int lane) {
+                                                  int64_t nb0, int jvalid, int lane,
+                                                  int i0 = 0, int i1 = WM) {
   static_assert(WN % 4 == 0, "whole 32-column MX blocks per wave");
   if (jvalid < WN) return;  // columns past N (N is a multiple of 256)
   const int g4 = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < WM; ++i) {
+  for (int i = 0; i < WM; ++i) { if (i < i0 || i >= i1) continue;
     if (i >= nvalid) continue;
     const int r = row_base + RS * i + (lane & 15);
     const bool live = r < row_end;
@@ -396,10 +398,11 @@ __device__ __forceinline__ void epilogue_fc1_mx_t(const GemmParams& p, const v4f
 template <int WM, int WN, int RS = 16>
 __device__ __forceinline__ void epilogue_fc1_bf16_t(const GemmParams& p, const v4f (&acc)[WM][WN],
                                                     int row_base, int row_end, int nvalid,
-                                                    int64_t nb0, int jvalid, int lane) {
+                                                    int64_t nb0, int jvalid, int lane,
+                                                    int i0 = 0, int i1 = WM) {
   const int c4 = 4 * (lane >> 4);
 #pragma unroll
-  for (int i = 0; i < WM; ++i) {
+  for (int i = 0; i < WM; ++i) { if (i < i0 || i >= i1) continue;
     if (i >= nvalid) continue;
     const int r = row_base + RS * i + (lane & 15);
     if (r >= row_end) continue;
@@ -422,20 +425,21 @@ __device__ __forceinline__ void epilogue_fc1_bf16_t(const GemmParams& p, const v
 template <int V, bool FC1, int WM, int WN, int RS = 16>
 __device__ __forceinline__ void finish_tile_t(const GemmParams& p, const v4f (&acc)[WM][WN],
                                               const float (&sc)[WM], int row_base, int row_end,
-                                              int nvalid, int64_t nb0, int jvalid, int lane) {
+                                              int nvalid, int64_t nb0, int jvalid, int lane,
+                                              int i0 = 0, int i1 = WM) {
   if constexpr (FC1 && a_blockscaled(V) && WN % 4 == 0) {
     if (p.q_out) {
-      epilogue_fc1_mx_t<a_fp4(V), WM, WN, RS>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+      epilogue_fc1_mx_t<a_fp4(V), WM, WN, RS>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane, i0, i1);
       return;
     }
   }
   if constexpr (FC1 && V == kMxfp4Bf16) {
     if (p.q_out) {
-      epilogue_fc1_bf16_t<WM, WN, RS>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane);
+      epilogue_fc1_bf16_t<WM, WN, RS>(p, acc, row_base, row_end, nvalid, nb0, jvalid, lane, i0, i1);
       return;
     }
   }
-  epilogue_t<FC1, WM, WN, RS>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
+  epilogue_t<FC1, WM, WN, RS>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane, i0, i1);
 }
 
 hipError_t launch_gemm_direct(int variant, bool fc1, int cfg, const GemmParams& p,

@@ -574,7 +574,7 @@ __device__ __forceinline__ void wait_barrier() {
 // One code path for full and partial tiles: the per-subtile checks are scalar
 // branches, which also keep the compiler from hoisting every fragment read of
 // a step (a branch-free full-tile path needed more than 256 registers here).
-template <int V, bool FC1, int WM>
+template <int V, bool FC1, int WM, bool PEEL>
 __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds, const Tile tile,
                                               const int nt) {
   using namespace dma;
@@ -829,6 +829,59 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
     wait_barrier<(S == 0 ? 2 * kBPW : kBPW)>();
   };
 
+  // The last K step issues no loads and overlaps the epilogue with its
+  // MFMAs: subtile i - 1's outputs are written while subtile i's MFMAs run.
+  auto last_step = [&](auto s_c, int ks, int bstage) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_c)::value;
+    // the only loads still in flight are copies of earlier steps' data
+    // issued one step ago (their step index is clamped); drain them
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint8_t* bs = b_at(bstage);
+    if constexpr (S == 0) {
+      const uint8_t* ss = sx_at(ks);
+#pragma unroll
+      for (int j = 0; j < WN; ++j) sx[j] = *reinterpret_cast<const uint32_t*>(ss + j * 256);
+    }
+    const uint8_t* sa = sa_at(ks);
+    const uint8_t* as = a_at(S & 1);
+    v8i bop[WN];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const uint4 b = *reinterpret_cast<const uint4*>(bs + j * 1024);
+      bop[j] = fp4_operand(b);
+    }
+    if constexpr (!A4) read_a(as, sa, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      if constexpr (!A4) {
+        if (i + 1 < WM) read_a(as, sa, i + 1, (i + 1) & 1);
+        if (cols && i < nvalid) {
+          const v8i aop = as_v8i(alo[i & 1], ahi[i & 1]);
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            acc[i][j] = mfma_wt<AF, S, MXA ? S : 0>(bop[j], aop, acc[i][j], (int)sx[j],
+                                                   MXA ? axr[i & 1] : 127);
+        }
+      } else {
+        if (cols && i < nvalid) {
+          const v8i aop = fp4_operand(*reinterpret_cast<const uint4*>(as + i * kSub));
+          const int ax = *reinterpret_cast<const int*>(sa + i * kSaSub);
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            acc[i][j] = mfma_wt<AF, S, MXA ? S : 0>(bop[j], aop, acc[i][j], (int)sx[j], ax);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (i > 0)
+        finish_tile_t<V, FC1, WM, WN, RS>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid,
+                                          lane, i - 1, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    finish_tile_t<V, FC1, WM, WN, RS>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane,
+                                      WM - 1, WM);
+  };
+
   // prologue: A and weights (and scales) of step 0, weights of step 1
   issue_as(0, 0);
   issue_a(0, 0);
@@ -837,30 +890,54 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& p, uint8_t* lds,
   issue_b(min(1, KS - 1), 1);
   wait_barrier<kBPW>();
   int ks = 0, bstage = 0;
-  for (; ks + 4 <= KS; ks += 4) {
+  if constexpr (PEEL) {
+    // K a multiple of 512 (whole 4-step groups): the last step, S = 3, is
+    // peeled so its MFMAs overlap the epilogue (a kernel of its own: with the
+    // remainder steps and a peeled step of every S in one body the compiler
+    // spilled 200+ bytes per lane)
+    for (; ks + 4 < KS; ks += 4) {
+      step(std::integral_constant<int, 0>{}, ks, bstage);
+      bstage = bstage == 2 ? 0 : bstage + 1;
+      step(std::integral_constant<int, 1>{}, ks + 1, bstage);
+      bstage = bstage == 2 ? 0 : bstage + 1;
+      step(std::integral_constant<int, 2>{}, ks + 2, bstage);
+      bstage = bstage == 2 ? 0 : bstage + 1;
+      step(std::integral_constant<int, 3>{}, ks + 3, bstage);
+      bstage = bstage == 2 ? 0 : bstage + 1;
+    }
     step(std::integral_constant<int, 0>{}, ks, bstage);
     bstage = bstage == 2 ? 0 : bstage + 1;
     step(std::integral_constant<int, 1>{}, ks + 1, bstage);
     bstage = bstage == 2 ? 0 : bstage + 1;
     step(std::integral_constant<int, 2>{}, ks + 2, bstage);
     bstage = bstage == 2 ? 0 : bstage + 1;
-    step(std::integral_constant<int, 3>{}, ks + 3, bstage);
-    bstage = bstage == 2 ? 0 : bstage + 1;
+    last_step(std::integral_constant<int, 3>{}, ks + 3, bstage);
+  } else {
+    for (; ks + 4 <= KS; ks += 4) {
+      step(std::integral_constant<int, 0>{}, ks, bstage);
+      bstage = bstage == 2 ? 0 : bstage + 1;
+      step(std::integral_constant<int, 1>{}, ks + 1, bstage);
+      bstage = bstage == 2 ? 0 : bstage + 1;
+      step(std::integral_constant<int, 2>{}, ks + 2, bstage);
+      bstage = bstage == 2 ? 0 : bstage + 1;
+      step(std::integral_constant<int, 3>{}, ks + 3, bstage);
+      bstage = bstage == 2 ? 0 : bstage + 1;
+    }
+    if (ks < KS) { step(std::integral_constant<int, 0>{}, ks, bstage); bstage = bstage == 2 ? 0 : bstage + 1; }
+    if (ks + 1 < KS) { step(std::integral_constant<int, 1>{}, ks + 1, bstage); bstage = bstage == 2 ? 0 : bstage + 1; }
+    if (ks + 2 < KS) step(std::integral_constant<int, 2>{}, ks + 2, bstage);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    finish_tile_t<V, FC1, WM, WN, RS>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
   }
-  if (ks < KS) { step(std::integral_constant<int, 0>{}, ks, bstage); bstage = bstage == 2 ? 0 : bstage + 1; }
-  if (ks + 1 < KS) { step(std::integral_constant<int, 1>{}, ks + 1, bstage); bstage = bstage == 2 ? 0 : bstage + 1; }
-  if (ks + 2 < KS) step(std::integral_constant<int, 2>{}, ks + 2, bstage);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  finish_tile_t<V, FC1, WM, WN, RS>(p, acc, sc, row_base, row_end, nvalid, nb0, jvalid, lane);
 }
 
-template <int V, bool FC1, int WM>
+template <int V, bool FC1, int WM, bool PEEL>
 __global__ __launch_bounds__(dma::kNW * kWave, 1) void k_gemm_dma(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[dma::Map<WM, a_blockscaled(V), a_fp4(V)>::kBytes];
   Tile tile;
   int nt;
   if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
-  gemm_dma_body<V, FC1, WM>(p, lds, tile, nt);
+  gemm_dma_body<V, FC1, WM, PEEL>(p, lds, tile, nt);
 }
 
 template <int V, bool FC1>
@@ -871,8 +948,12 @@ static hipError_t launch_v(int cfg, const GemmParams& p, int64_t blocks, hipStre
     if constexpr (V == kInt4Fp8) k_gemm_lds<V, FC1, 8, 1, 4, 4, 1><<<(unsigned)blocks, 512, 0, st>>>(p);
     else k_gemm_lds<V, FC1, 4, 1, 4, 4><<<(unsigned)blocks, 256, 0, st>>>(p);
   }
-  else if constexpr (scaled_fp4(V))  // 160 x 512
-    k_gemm_dma<V, FC1, 5><<<(unsigned)blocks, dma::kNW * kWave, 0, st>>>(p);
+  else if constexpr (scaled_fp4(V)) {  // 160 x 512
+    if (p.K % (4 * kKStep) == 0)  // whole 4-step groups: peeled last step
+      k_gemm_dma<V, FC1, 5, true><<<(unsigned)blocks, dma::kNW * kWave, 0, st>>>(p);
+    else
+      k_gemm_dma<V, FC1, 5, false><<<(unsigned)blocks, dma::kNW * kWave, 0, st>>>(p);
+  }
   else k_gemm_ab<V, FC1, 8, 2, 4, 4><<<(unsigned)blocks, 512, 0, st>>>(p);
   return hipGetLastError();
 }
