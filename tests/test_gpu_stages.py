@@ -34,6 +34,10 @@ ROUTE_CASES = [
     (257, 16, 4, 0.0, 0.5, 106),    # logits on a 0.5 grid: many exact ties
     (130, 1024, 16, 0.0, 0.25, 107),  # the most experts and the largest top-k, with ties
     (5, 3, 3, 0.0, 0.0, 108),       # k = E
+    (1024, 256, 8, 0.0, 0.0, 109),  # the INT4 batch (16 chunks)
+    (1025, 256, 8, 0.0, 0.0, 110),  # a last chunk of one token
+    (700, 1024, 2, 0.0, 0.25, 111),  # 11 chunks x 1024 experts, ties
+    (500, 128, 4, 2.0, 0.5, 112),   # 8 chunks, skewed, ties
 ]
 
 
