@@ -529,7 +529,8 @@ __global__ __launch_bounds__(kWave * NW, MINB) void k_gemm_ab(GemmParams p) {
 // assembly: the compiler does not track them, which keeps its conservative
 // full drains out of the loop; the kernel drains them itself before the
 // epilogue (an LDS write landing after the block exits would corrupt the next
-// block's LDS).
+// block's LDS): at the start of the peeled last step when K is a multiple of
+// 512, else after the last step.
 namespace dma {
 constexpr int kNW = 8, kWN = 8, kWavesN = 4;
 constexpr int kBNB = kWavesN * kWN;     // 16-column blocks per tile
