@@ -254,22 +254,47 @@ __device__ __forceinline__ void store4(float* dst, float x, float y, float z, fl
 }
 
 // FC1: h = silu(g * s) * (u * s) for tiles (2q, 2q+1) = gate / up of
-// intermediate block (nb0 + 2q) / 2, streaming stores; FC2: y2 = acc * s,
-// plain (cached) stores.  Same-box timings of the prefill GEMMs with 16-byte
-// stores: plain y2 stores made GEMM2 6 % faster on both DeepSeek prefill
-// shapes, plain h stores made the 4096-token GEMM1 6 % slower.
-// A lane holds 4 columns of one row, so a 16-byte store covers 16 rows x 64
-// bytes.  For h, the lanes of rows r and r ^ 8 swap the halves of two
-// neighbouring h subtiles first, so each store writes 8 rows x 128 bytes,
-// whole cache lines (GEMM1 1.3 % faster on both prefill shapes; the same
-// exchange for the y2 stores changed nothing).
+// intermediate block (nb0 + 2q) / 2; FC2: y2 = acc * s.  A lane holds 4
+// columns of one row, so a 16-byte store covers 16 rows x 64 bytes; the lanes
+// of rows r and r ^ 8 first swap the halves of two neighbouring subtiles, so
+// each store writes 8 rows x 128 bytes, whole cache lines, and both outputs
+// leave with streaming stores.  Same-box timings on the DeepSeek prefill
+// shapes: whole lines made GEMM1 1.3 % faster; for y2, streaming stores were
+// 6 % slower than plain ones with half lines and are 1.4 % faster with whole
+// lines (and the finalize that reads y2 back 2-4 % faster).  Subtiles
+// [i0, i1) only (the peeled last K step writes them one by one).
 template <bool FC1, int WM, int WN, int RS = 16>
 __device__ __forceinline__ void epilogue_t(const GemmParams& p, const v4f (&acc)[WM][WN],
                                            const float (&sc)[WM], int row_base, int row_end,
                                            int nvalid, int64_t nb0, int jvalid, int lane,
                                            int i0 = 0, int i1 = WM) {
   const int c4 = 4 * (lane >> 4);
-  if constexpr (FC1 && WN % 4 == 0) {
+  if constexpr (!FC1 && WN % 2 == 0) {
+    const bool lo = (lane & 8) == 0;
+    const int rr = lane & 7;
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      if (i >= nvalid) continue;
+      if (i < i0 || i >= i1) continue;
+      const float s = sc[i];
+      const int r0 = row_base + RS * i;
+#pragma unroll
+      for (int j = 0; j < WN; j += 2) {
+        if (j >= jvalid) continue;
+        const v4f a0 = acc[i][j] * s, a1 = acc[i][j + 1] * s;
+        const v4f snd = lo ? a1 : a0;
+        v4f rcv;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) rcv[c] = __shfl_xor(snd[c], 8);
+        const int64_t col = (nb0 + j + (lo ? 0 : 1)) * 16 + c4;
+        const v4f v0 = lo ? a0 : rcv, v1 = lo ? rcv : a1;
+        if (r0 + rr < row_end)
+          store4_nt(p.out + (int64_t)(r0 + rr) * p.out_stride + col, v0[0], v0[1], v0[2], v0[3]);
+        if (r0 + 8 + rr < row_end)
+          store4_nt(p.out + (int64_t)(r0 + 8 + rr) * p.out_stride + col, v1[0], v1[1], v1[2], v1[3]);
+      }
+    }
+  } else if constexpr (FC1 && WN % 4 == 0) {
     const bool lo = (lane & 8) == 0;
     const int rr = lane & 7;
 #pragma unroll
