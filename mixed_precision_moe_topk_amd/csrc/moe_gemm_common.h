@@ -149,46 +149,109 @@ __device__ __forceinline__ void load_row_scales(const GemmParams& p, int row_bas
     }
 }
 
+// 4 x 4 transpose inside each quad of lanes (DPP quad permutes): on entry
+// lane 4a + b holds m[v] = M[b][v], on exit M[v][b].  Swapping bit 0 and then
+// bit 1 of (lane, value) transposes the 2-bit indices.
+__device__ __forceinline__ v4f quad_transpose(const v4f& m, int lane) {
+  const int b = lane & 3;
+  v4f t, r;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float x = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m[v ^ 1]), 0xB1, 0xF, 0xF, false));
+    t[v] = ((b ^ v) & 1) ? x : m[v];
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float x = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(t[v ^ 2]), 0x4E, 0xF, 0xF, false));
+    r[v] = ((b ^ v) & 2) ? x : t[v];
+  }
+  return r;
+}
+
+// Row-per-register epilogue (INT4): lane l of tile (i, j) holds rows
+// 4 (l / 16) + [0, 4) of column l % 16.  The four lanes of a quad transpose
+// their 4 x 4 block first, so each holds four consecutive columns of one row,
+// and two neighbouring subtiles leave as whole 128-byte lines with 16-byte
+// streaming stores (same box: INT4 GEMM2 0.424 -> 0.411 ms; the transpose
+// alone, 16 rows x 64 bytes per store, changed nothing).
 template <bool FC1, int WM, int WN, int RS = 16>
 __device__ __forceinline__ void epilogue_sc(const GemmParams& p, const v4f (&acc)[WM][WN],
                                             const float (&sc)[WM][4], int row_base, int row_end,
                                             int nvalid, int64_t nb0, int jvalid, int lane) {
-  const int col_lane = lane & 15;
   const int row_lane = 4 * (lane >> 4);
-  if (FC1) {
+  const int rq = lane & 3;                 // row of the quad's block after the transpose
+  const int cq = 4 * ((lane & 15) >> 2);   // its first column
+  // output subtile pairs: lanes of rows 8-15 (lane bit 5) swap their first
+  // block for the second block of rows 0-7, so each store writes 8 rows x
+  // 128 bytes (one pair of 16-column h blocks for FC1, of y2 subtiles for FC2)
+  const bool lo = (lane & 32) == 0;
+  const int rbase = 4 * ((lane >> 4) & 1) + rq;  // row within the 8-row half
+  auto store_pair = [&](int i, const v4f& y0, const v4f& y1, int64_t col0)
+                        __attribute__((always_inline)) {
+    const v4f t0 = quad_transpose(y0, lane), t1 = quad_transpose(y1, lane);
+    const v4f snd = lo ? t1 : t0;
+    v4f rcv;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) rcv[c] = __shfl_xor(snd[c], 32);
+    const int64_t col = col0 + (lo ? 0 : 16) + cq;
+    const v4f va = lo ? t0 : rcv, vb = lo ? rcv : t1;
+    const int ra = row_base + RS * i + rbase, rb = ra + 8;
+    if (ra < row_end)
+      __builtin_nontemporal_store(va, reinterpret_cast<v4f*>(&p.out[(int64_t)ra * p.out_stride + col]));
+    if (rb < row_end)
+      __builtin_nontemporal_store(vb, reinterpret_cast<v4f*>(&p.out[(int64_t)rb * p.out_stride + col]));
+  };
+  if constexpr (FC1 && WN % 4 != 0) {
+    // one h block per wave: 16 rows x 64 bytes per store
 #pragma unroll
     for (int q = 0; q < WN / 2; ++q) {
       if (2 * q >= jvalid) continue;
-      const int64_t ib = (nb0 + 2 * q) >> 1;  // intermediate 16-column block
-      const int64_t c = ib * 16 + col_lane;
+      const int64_t ib = (nb0 + 2 * q) >> 1;
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
         if (i >= nvalid) continue;
+        v4f h;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          h[v] = silu(acc[i][2 * q][v] * sc[i][v]) * (acc[i][2 * q + 1][v] * sc[i][v]);
+        const v4f t = quad_transpose(h, lane);
+        const int r = row_base + RS * i + row_lane + rq;
+        if (r < row_end)
+          __builtin_nontemporal_store(t, reinterpret_cast<v4f*>(&p.out[(int64_t)r * p.out_stride + ib * 16 + cq]));
+      }
+    }
+  } else if constexpr (FC1) {
+#pragma unroll
+    for (int q = 0; q < WN / 2; q += 2) {
+      if (2 * q >= jvalid) continue;
+      const int64_t ib = (nb0 + 2 * q) >> 1;  // first of two intermediate 16-column blocks
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        if (i >= nvalid) continue;
+        v4f h0, h1;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int r = row_base + RS * i + row_lane + v;
-          if (r < row_end) {
-            const float g = acc[i][2 * q][v] * sc[i][v];
-            const float u = acc[i][2 * q + 1][v] * sc[i][v];
-            __builtin_nontemporal_store(silu(g) * u, &p.out[(int64_t)r * p.out_stride + c]);
-          }
+          h0[v] = silu(acc[i][2 * q][v] * sc[i][v]) * (acc[i][2 * q + 1][v] * sc[i][v]);
+          h1[v] = silu(acc[i][2 * q + 2][v] * sc[i][v]) * (acc[i][2 * q + 3][v] * sc[i][v]);
         }
+        store_pair(i, h0, h1, ib * 16);
       }
     }
   } else {
+    static_assert(WN % 2 == 0, "pairs of y2 subtiles");
 #pragma unroll
-    for (int j = 0; j < WN; ++j) {
+    for (int j = 0; j < WN; j += 2) {
       if (j >= jvalid) continue;
-      const int64_t c = (nb0 + j) * 16 + col_lane;
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
         if (i >= nvalid) continue;
+        v4f y0, y1;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int r = row_base + RS * i + row_lane + v;
-          if (r < row_end)
-            __builtin_nontemporal_store(acc[i][j][v] * sc[i][v], &p.out[(int64_t)r * p.out_stride + c]);
+          y0[v] = acc[i][j][v] * sc[i][v];
+          y1[v] = acc[i][j + 1][v] * sc[i][v];
         }
+        store_pair(i, y0, y1, (nb0 + j) * 16);
       }
     }
   }
