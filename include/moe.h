@@ -283,8 +283,9 @@ moe_status moe_set_fc2_fused(int32_t enable);
  *                   (token, slot)
  *   workspace:      device buffer of at least moe_workspace_query bytes for
  *                   the same dims, num_tokens and top_k; the routing scratch
- *                   (per-chunk counts) and the GEMM work map are written to its
- *                   chunk_counts, tiles and num_tiles regions (moe_ws_layout)
+ *                   (per-chunk and per-group counts) and the GEMM work map
+ *                   are written to its chunk_counts, tiles and num_tiles
+ *                   regions (moe_ws_layout)
  * The outputs may lie inside the workspace at the offsets moe_workspace_layout
  * gives for them (where moe_run_ws puts them).  num_tokens = 0 returns MOE_OK
  * without launching.  Errors as moe_run_ws. */

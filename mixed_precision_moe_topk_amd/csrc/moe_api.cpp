@@ -198,7 +198,7 @@ moe_status layout_of(const moe_dims* d, int64_t T, int32_t k, moe_ws_layout* L, 
   std::memset(L, 0, sizeof(*L));
   L->ids = take(rows * 4);
   L->topk_w = take(rows * 4);
-  L->chunk_counts = take(nchunks * E * 4);
+  L->chunk_counts = take((nchunks + cdiv(nchunks, moe::kRouteGroupChunks)) * E * 4);
   L->offsets = take((E + 1) * 4);
   L->row_token = take(rows * 4);
   L->slot_row = take(rows * 4);

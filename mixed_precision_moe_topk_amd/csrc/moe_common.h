@@ -13,6 +13,7 @@ constexpr int kKStep = 128;        // K consumed by one 16x16x128 MFMA
 constexpr int kMxBlock = 32;       // elements per E8M0 scale (OCP MX block)
 constexpr int kInt4Group = 128;    // elements per INT4 group scale
 constexpr int kRouteChunkTokens = 64;  // tokens per routing chunk (one wave)
+constexpr int kRouteGroupChunks = 16;  // chunks per block of the routing count kernel
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 1024;
 
@@ -169,7 +170,7 @@ struct RouteParams {
   int32_t top_k;
   int32_t* ids;            // [T, k]
   float* weights;          // [T, k]
-  int32_t* chunk_counts;   // [nchunks, E]
+  int32_t* chunk_counts;   // [nchunks, E] then the group counts [ngroups, E]
   int32_t nchunks;         // ceil(T / kRouteChunkTokens)
   int32_t* offsets;        // [E + 1]
   int32_t* row_token;      // [T*k]

@@ -16,35 +16,87 @@
 // grid indexes it with a 64-bit linear block index.
 #include "moe_common.h"
 
-// Wave-wide reductions of the ROCm device library (results in every lane).
-extern "C" __device__ __attribute__((const)) float __ockl_wfred_max_f32(float);
-extern "C" __device__ __attribute__((const)) int __ockl_wfred_min_i32(int);
+// Wave-wide reduction of the ROCm device library (result in every lane).
+extern "C" __device__ __attribute__((const)) uint32_t __ockl_wfred_max_u32(uint32_t);
 
 namespace moe {
 
+// Order-preserving code of a logit: the larger code is the larger logit.
+// NaN codes as -inf and -0.0 as +0.0, so equal logits (either zero) tie and
+// the expert index decides.  Every logit codes to at least 0x007FFFFF (-inf),
+// so code 0 marks an empty slot.
+__device__ __forceinline__ uint32_t logit_code(float x) {
+  const uint32_t u = __float_as_uint(x == x ? x + 0.0f : -INFINITY);
+  return (u >> 31) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float code_logit(uint32_t c) {
+  return __uint_as_float((c >> 31) ? (c & 0x7FFFFFFFu) : ~c);
+}
+
+// Lanes set in m take b, the others a (two v_cndmask; written as asm so that
+// a chain of them over an array stays a chain of selects instead of being
+// rewritten into a data-dependent index with a select tree per element).
+__device__ __forceinline__ uint64_t pick64(uint64_t a, uint64_t b, uint64_t m) {
+  uint32_t lo, hi;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3"
+      : "=v"(lo) : "v"((uint32_t)a), "v"((uint32_t)b), "s"(m));
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3"
+      : "=v"(hi) : "v"((uint32_t)(a >> 32)), "v"((uint32_t)(b >> 32)), "s"(m));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Batcher's merge-exchange sorting network for N keys (Knuth, TAOCP vol. 3,
+// 5.2.2 Algorithm M), valid for any N: 12 comparators for 6 keys, 19 for 8.
+template <int N>
+struct MergeExchange {
+  int a[N * N + 1], b[N * N + 1];
+  int n;
+  constexpr MergeExchange() : a(), b(), n(0) {
+    int t = 0;
+    while ((1 << t) < N) ++t;
+    for (int p = t > 0 ? 1 << (t - 1) : 0; p > 0; p >>= 1) {
+      int q = 1 << (t - 1), r = 0, d = p;
+      for (;;) {
+        for (int i = 0; i + d < N; ++i)
+          if ((i & p) == r) {
+            a[n] = i;
+            b[n] = i + d;
+            ++n;
+          }
+        if (q == p) break;
+        d = q - p;
+        q >>= 1;
+        r = p;
+      }
+    }
+  }
+};
+
 // Top-k and softmax of token t, by one wave.  Lane j holds logits j, j+64,
-// ..., PER of them (E <= 64 PER).  Each of the k rounds takes every lane's
-// best remaining logit (larger value, then smaller expert index), the wave
-// maximum of those by a reduction, and the lanes that hold the maximum by a
-// ballot; if more than one lane holds it (an exact tie, or -0.0 against
-// +0.0), the smallest expert index among them wins, by a second reduction.
-// A round is thus a chain of two or three wave reductions instead of a
-// six-step shuffle of value and index.
+// ..., PER of them (E <= 64 PER), as 64-bit keys (code << 32 | ~expert: the
+// larger key is the larger logit, then the smaller expert index), sorted in
+// descending order once.  Each of the k rounds then takes the wave maximum
+// of the lanes' first codes by one integer reduction; the lane that holds it
+// (by a ballot; on an exact tie, the one with the smaller expert index, by a
+// second reduction) gives up its first key.
 template <int PER>
 __device__ __forceinline__ void route_token(const RouteParams& p, const int64_t t) {
   const int lane = lane_id();
   const int E = p.experts;
   const float* row = p.logits + t * E;
-  float v[PER];
-  uint32_t taken = 0;  // bit i: value i of this lane already selected (or absent)
+  uint64_t key[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + i * kWave;
-    const float x = (e < E) ? row[e] : 0.0f;
-    // a NaN logit ranks as -inf: every round then has a holder of the
-    // maximum (-inf at worst), so every id is a valid expert index
-    v[i] = x == x ? x : -INFINITY;
-    if (e >= E) taken |= 1u << i;
+    key[i] = e < E ? ((uint64_t)logit_code(row[e]) << 32) | (uint32_t)~e : 0;
+  }
+  constexpr MergeExchange<PER> net{};
+#pragma unroll
+  for (int c = 0; c < net.n; ++c) {
+    const uint64_t x = key[net.a[c]], y = key[net.b[c]];
+    const bool s = y > x;
+    key[net.a[c]] = s ? y : x;
+    key[net.b[c]] = s ? x : y;
   }
 
   float sel_v[kMaxTopK];
@@ -55,43 +107,43 @@ __device__ __forceinline__ void route_token(const RouteParams& p, const int64_t 
     sel_v[j] = 0.0f;
     sel_e[j] = 0;
     if (j >= K) continue;
-    // lane-local best: larger value, then smaller expert index
-    float bv = -INFINITY;
-    int be = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (taken & (1u << i)) continue;
-      if (be == 0x7FFFFFFF || v[i] > bv) {  // indices grow with i: ties keep the first
-        bv = v[i];
-        be = lane + i * kWave;
-      }
-    }
-    const float vmax = __ockl_wfred_max_f32(bv);
-    const bool hold = be != 0x7FFFFFFF && bv == vmax;
+    // at least E - j >= 1 logits remain, so cmax is a logit's code (> 0)
+    const uint32_t hc = (uint32_t)(key[0] >> 32);
+    const uint32_t cmax = __ockl_wfred_max_u32(hc);
+    const bool hold = hc == cmax;
     const uint64_t holders = __ballot(hold);
-    int win;
-    if (__popcll(holders) == 1)
-      win = __builtin_amdgcn_readlane(be, __ffsll((unsigned long long)holders) - 1);
-    else
-      win = __ockl_wfred_min_i32(hold ? be : 0x7FFFFFFF);
-    sel_v[j] = vmax;
-    sel_e[j] = win;
-    if ((win & (kWave - 1)) == lane) taken |= 1u << (win / kWave);
-  }
-  // softmax over the selected logits (sel_v[0] is the largest)
-  float sum = 0.0f;
-  float pr[kMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    pr[j] = (j < K) ? expf(sel_v[j] - sel_v[0]) : 0.0f;
-    sum += pr[j];
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j < K && lane == j) {
-      p.ids[t * K + j] = sel_e[j];
-      p.weights[t * K + j] = __fdiv_rn(pr[j], sum);
+    int wl;
+    if (__popcll(holders) == 1) {
+      wl = __ffsll((unsigned long long)holders) - 1;
+    } else {  // equal logits: the largest ~expert, i.e. the smallest expert
+      const uint32_t lo = __ockl_wfred_max_u32(hold ? (uint32_t)key[0] : 0u);
+      wl = __ffsll((unsigned long long)__ballot(hold && (uint32_t)key[0] == lo)) - 1;
     }
+    sel_v[j] = code_logit(cmax);
+    sel_e[j] = (int)~(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key[0], wl);
+    const uint64_t w = 1ull << wl;  // the winning lane shifts its keys up by one
+#pragma unroll
+    for (int i = 0; i + 1 < PER; ++i) key[i] = pick64(key[i], key[i + 1], w);
+    key[PER - 1] = pick64(key[PER - 1], 0, w);
+  }
+  // softmax over the selected logits (sel_v[0] is the largest): lane j < k
+  // takes slot j's exponential; the sum runs over the slots in order
+  float lv = 0.0f;
+  int le = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (lane == j) {
+      lv = sel_v[j];
+      le = sel_e[j];
+    }
+  const float pj = lane < K ? expf(lv - sel_v[0]) : 0.0f;
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pj), j));
+  if (lane < K) {
+    p.ids[t * K + lane] = le;
+    p.weights[t * K + lane] = __fdiv_rn(pj, sum);
   }
 }
 
@@ -122,12 +174,15 @@ __device__ __forceinline__ void build_masks(const RouteParams& p, uint64_t* mask
   __syncthreads();
 }
 
-__global__ __launch_bounds__(64) void k_route_count(RouteParams p) {
-  __shared__ uint64_t mask[kMaxExperts];
-  build_masks(p, mask, (int64_t)blockIdx.x * kChunkTokens);
-  for (int e = lane_id(); e < p.experts; e += kWave)
-    p.chunk_counts[(int64_t)blockIdx.x * p.experts + e] = __popcll(mask[e]);
-}
+// The count kernel takes kGroupChunks chunks per block (one wave each), so
+// the single-block scan runs over groups of chunks (16 groups for 16384
+// tokens instead of 256 chunks: the scan's chain of dependent loads shrinks
+// accordingly).  Per expert it writes, for each chunk, the rows in earlier
+// chunks of its group (chunk_counts) and the group's total (group counts,
+// stored after the chunk counts).
+constexpr int kGroupChunks = kRouteGroupChunks;
+static_assert(kGroupChunks * kWave == 1024 && kMaxExperts <= 1024,
+              "one count-kernel thread per expert (its scan for a single group)");
 
 // Single block: per-expert totals, chunk bases, expert offsets, tile list.
 // Thread e (blockDim.x == 1024 >= E) holds `run`, the rows of expert e.
@@ -169,23 +224,49 @@ __device__ int32_t scan_experts(const RouteParams& p, const int32_t run, int32_t
   return ex_a;
 }
 
+// A batch of one group (at most 1024 tokens) also runs the scan here, so its
+// routing index takes two launches instead of three.
+__global__ __launch_bounds__(kGroupChunks * kWave) void k_route_count(RouteParams p) {
+  __shared__ uint64_t gmask[kGroupChunks][kMaxExperts];
+  __shared__ int32_t wsum[2][16];
+  const int w = threadIdx.x / kWave;
+  const int64_t c0 = (int64_t)blockIdx.x * kGroupChunks;
+  build_masks(p, gmask[w], (c0 + w) * kChunkTokens);
+  const int E = p.experts;
+  const int e = threadIdx.x;  // blockDim.x == 1024 >= E
+  const bool single = gridDim.x == 1;
+  int32_t* group_counts = p.chunk_counts + (int64_t)p.nchunks * E;
+  int32_t run = 0;
+  if (e < E) {
+#pragma unroll
+    for (int u = 0; u < kGroupChunks; ++u) {
+      if (c0 + u < p.nchunks) p.chunk_counts[(c0 + u) * E + e] = run;
+      run += __popcll(gmask[u][e]);
+    }
+    // one group: its prefix (rows in earlier groups) is 0
+    group_counts[(int64_t)blockIdx.x * E + e] = single ? 0 : run;
+  }
+  if (single) scan_experts(p, run, wsum);
+}
+
 __global__ __launch_bounds__(1024) void k_route_scan(RouteParams p) {
   __shared__ int32_t wsum[2][16];
   const int E = p.experts;
   const int e = threadIdx.x;  // blockDim.x == 1024 >= E
+  const int64_t ng = (p.nchunks + kGroupChunks - 1) / kGroupChunks;
+  int32_t* group_counts = p.chunk_counts + (int64_t)p.nchunks * E;
   int32_t run = 0;
   if (e < E) {
-    // exclusive prefix over chunks, 16 independent loads at a time (a chain
-    // of dependent loads would cost one memory latency per chunk)
+    // exclusive prefix over groups, 16 independent loads at a time (a chain
+    // of dependent loads would cost one memory latency per group)
     constexpr int kB = 16;
-    for (int c0 = 0; c0 < p.nchunks; c0 += kB) {
+    for (int64_t g0 = 0; g0 < ng; g0 += kB) {
       int32_t v[kB];
 #pragma unroll
-      for (int u = 0; u < kB; ++u)
-        v[u] = c0 + u < p.nchunks ? p.chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
+      for (int u = 0; u < kB; ++u) v[u] = g0 + u < ng ? group_counts[(g0 + u) * E + e] : 0;
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
-        if (c0 + u < p.nchunks) p.chunk_counts[(int64_t)(c0 + u) * E + e] = run;  // rows in earlier chunks
+        if (g0 + u < ng) group_counts[(g0 + u) * E + e] = run;  // rows in earlier groups
         run += v[u];
       }
     }
@@ -204,8 +285,9 @@ __global__ __launch_bounds__(64) void k_route_scatter(RouteParams p) {
   for (int j = 0; j < p.top_k; ++j) {
     const int64_t f = t * p.top_k + j;
     const int e = p.ids[f];
-    const int pos = p.offsets[e] + p.chunk_counts[(int64_t)blockIdx.x * p.experts + e] +
-                    __popcll(mask[e] & below);
+    const int pos = p.offsets[e] +
+                    p.chunk_counts[((int64_t)p.nchunks + blockIdx.x / kGroupChunks) * p.experts + e] +
+                    p.chunk_counts[(int64_t)blockIdx.x * p.experts + e] + __popcll(mask[e] & below);
     p.row_token[pos] = (int32_t)t;
     p.slot_row[f] = pos;
   }
@@ -250,15 +332,19 @@ hipError_t launch_route(const RouteParams& p, hipStream_t st) {
   // logits per lane: the fewest that hold all experts
   if (p.experts <= 64) k_router<1><<<grid, block, 0, st>>>(p);
   else if (p.experts <= 128) k_router<2><<<grid, block, 0, st>>>(p);
+  else if (p.experts <= 192) k_router<3><<<grid, block, 0, st>>>(p);
   else if (p.experts <= 256) k_router<4><<<grid, block, 0, st>>>(p);
+  else if (p.experts <= 384) k_router<6><<<grid, block, 0, st>>>(p);
   else if (p.experts <= 512) k_router<8><<<grid, block, 0, st>>>(p);
+  else if (p.experts <= 768) k_router<12><<<grid, block, 0, st>>>(p);
   else k_router<16><<<grid, block, 0, st>>>(p);
   if (p.tokens <= kChunkTokens) {
     k_route_small<<<1, 1024, 0, st>>>(p);
     return hipGetLastError();
   }
-  k_route_count<<<p.nchunks, 64, 0, st>>>(p);
-  k_route_scan<<<1, 1024, 0, st>>>(p);
+  const int ngroups = (p.nchunks + kGroupChunks - 1) / kGroupChunks;
+  k_route_count<<<ngroups, kGroupChunks * kWave, 0, st>>>(p);
+  if (ngroups > 1) k_route_scan<<<1, 1024, 0, st>>>(p);
   k_route_scatter<<<p.nchunks, 64, 0, st>>>(p);
   return hipGetLastError();
 }
