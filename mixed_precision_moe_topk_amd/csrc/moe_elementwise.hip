@@ -233,16 +233,19 @@ __global__ __launch_bounds__(256) void k_quant_mx(const void* __restrict__ src, 
 
 // Blocks (t, y): out[t] = bf16(sum_j fl32(w[t,j] * y2[row(t,j)])), the float32
 // sum taken in slot order, over the float4 columns y, y + gridDim.y, ... (in
-// units of 256).  H % 4 == 0.  A block walks its k rows from start to end, so
-// each row is read as one sequential stream.  KC > 0: top-k known at
-// compile time, so the k row loads of a column group are issued together
+// units of the block size).  H % 4 == 0.  A block walks its k rows from start
+// to end, so each row is read as one sequential stream.  KC > 0: top-k known
+// at compile time, so the k row loads of a column group are issued together
 // (one load in flight per thread would leave the kernel latency-bound).
-template <int KC>
-__global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ y2,
+template <int KC, int NTHR>
+__global__ __launch_bounds__(NTHR) void k_finalize(const float* __restrict__ y2,
                                                   const float* __restrict__ weights,
                                                   const int32_t* __restrict__ slot_row,
                                                   int32_t k_rt, int32_t H,
                                                   uint16_t* __restrict__ out) {
+  // each product is rounded to float32 before it is added: no fused
+  // multiply-add (by default the compiler contracts w * y + acc into one)
+#pragma clang fp contract(off)
   const int64_t t = blockIdx.x;
   const int k = KC > 0 ? KC : k_rt;
   const int nv = H / 4;
@@ -257,19 +260,19 @@ __global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ y2,
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
         const float w = weights[t * KC + j];
-        acc.x = __fadd_rn(acc.x, __fmul_rn(w, y[j].x));
-        acc.y = __fadd_rn(acc.y, __fmul_rn(w, y[j].y));
-        acc.z = __fadd_rn(acc.z, __fmul_rn(w, y[j].z));
-        acc.w = __fadd_rn(acc.w, __fmul_rn(w, y[j].w));
+        acc.x = acc.x + w * y[j].x;
+        acc.y = acc.y + w * y[j].y;
+        acc.z = acc.z + w * y[j].z;
+        acc.w = acc.w + w * y[j].w;
       }
     } else {
       for (int j = 0; j < k; ++j) {
         const float w = weights[t * k + j];
         const float4 y = load_stream(reinterpret_cast<const float4*>(y2 + (int64_t)slot_row[t * k + j] * H) + i);
-        acc.x = __fadd_rn(acc.x, __fmul_rn(w, y.x));
-        acc.y = __fadd_rn(acc.y, __fmul_rn(w, y.y));
-        acc.z = __fadd_rn(acc.z, __fmul_rn(w, y.z));
-        acc.w = __fadd_rn(acc.w, __fmul_rn(w, y.w));
+        acc.x = acc.x + w * y.x;
+        acc.y = acc.y + w * y.y;
+        acc.z = acc.z + w * y.z;
+        acc.w = acc.w + w * y.w;
       }
     }
     reinterpret_cast<uint2*>(out + t * H)[i] =
@@ -302,18 +305,32 @@ hipError_t launch_requant(const float* h, int64_t rows, int32_t I, int mode, uin
 hipError_t launch_finalize(const float* y2, const float* weights, const int32_t* slot_row,
                            int64_t T, int32_t k, int32_t H, uint16_t* out, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  // a block of 256 threads walks a token's H/4 float4 columns; with few
-  // tokens the columns are split over up to 2048 / T blocks per token so that
-  // a small batch still fills the GPU (64 tokens, H = 7168: 7 blocks each)
+  // Many tokens: a block of 1024 threads per token (3 % faster than 256 on
+  // 16384 tokens x 7168 columns; the output stores, not the y2 reads, set the
+  // pace: without them the kernel reads at a plain read's 7.1 TB/s).  Few
+  // tokens: 256 threads, with a token's columns split over up to 2048 / T
+  // blocks so that a small batch still fills the GPU (64 tokens, H = 7168: 7
+  // blocks each).
+  if (T >= 2048) {
+    const dim3 grid((unsigned)T, 1);
+    switch (k) {
+      case 2: k_finalize<2, 1024><<<grid, 1024, 0, st>>>(y2, weights, slot_row, k, H, out); break;
+      case 4: k_finalize<4, 1024><<<grid, 1024, 0, st>>>(y2, weights, slot_row, k, H, out); break;
+      case 6: k_finalize<6, 1024><<<grid, 1024, 0, st>>>(y2, weights, slot_row, k, H, out); break;
+      case 8: k_finalize<8, 1024><<<grid, 1024, 0, st>>>(y2, weights, slot_row, k, H, out); break;
+      default: k_finalize<0, 1024><<<grid, 1024, 0, st>>>(y2, weights, slot_row, k, H, out); break;
+    }
+    return hipGetLastError();
+  }
   const int64_t nchunk = (H / 4 + 255) / 256;
   const int64_t split = std::max<int64_t>(1, std::min<int64_t>(nchunk, 2048 / std::max<int64_t>(T, 1)));
   const dim3 grid((unsigned)T, (unsigned)split);
   switch (k) {
-    case 2: k_finalize<2><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
-    case 4: k_finalize<4><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
-    case 6: k_finalize<6><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
-    case 8: k_finalize<8><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
-    default: k_finalize<0><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
+    case 2: k_finalize<2, 256><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
+    case 4: k_finalize<4, 256><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
+    case 6: k_finalize<6, 256><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
+    case 8: k_finalize<8, 256><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
+    default: k_finalize<0, 256><<<grid, 256, 0, st>>>(y2, weights, slot_row, k, H, out); break;
   }
   return hipGetLastError();
 }

@@ -15,4 +15,4 @@ of the pages pins the whole-layer output ("parity unpinned" against the
 pages themselves; pinned against definitions and invariants).
 """
 from . import formats, quant, layer  # noqa: F401
-from .layer import route, expand, forward, quantize_expert, ExpertWeights  # noqa: F401
+from .layer import route, expand, forward, finalize, quantize_expert, ExpertWeights  # noqa: F401

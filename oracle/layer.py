@@ -121,6 +121,21 @@ def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     return (g / (1.0 + np.exp(-g)) * u.astype(np.float64)).astype(np.float32)
 
 
+def finalize(w: np.ndarray, y2: np.ndarray, slot_row: np.ndarray):
+    """The router-weighted top-k reduction after GEMM2 (PR #4793, the
+    finalize step that consumes token_final_scales): out[t] =
+    bf16(sum_j fl32(w[t,j] * y2[slot_row[t,j]])), each product rounded to
+    float32 and the sum kept in float32, taken in slot order.  w float32
+    [T, k], y2 float32 [rows, H], slot_row [T, k].  Returns (bf16 bits
+    uint16 [T, H], the float32 sum)."""
+    t, k = w.shape
+    acc = np.zeros((t, y2.shape[1]), dtype=np.float32)
+    for j in range(k if t else 0):
+        term = (w[:, j:j + 1] * y2[slot_row[:, j]]).astype(np.float32)
+        acc = (acc + term).astype(np.float32)
+    return F.bf16_rne(acc), acc
+
+
 def forward(hidden_bits: np.ndarray, logits: np.ndarray, top_k: int,
             expert_fn: Callable[[int], ExpertWeights], wfmt: str, afmt: str,
             check_exact: bool = True, keep_y1: bool = False,
@@ -222,11 +237,7 @@ def forward(hidden_bits: np.ndarray, logits: np.ndarray, top_k: int,
         y2[r0:r1] = (acc2 * ss[:, None].astype(np.float64)).astype(np.float32)
     if y2 is None:  # no expert pass ran (empty batch, or an empty only_experts)
         y2 = np.zeros((rows, h), dtype=np.float32)
-    acc_out = np.zeros((t, h), dtype=np.float32)
-    for j in range(top_k if t else 0):
-        term = (w[:, j:j + 1] * y2[slot_row[:, j]]).astype(np.float32)
-        acc_out = (acc_out + term).astype(np.float32)
-    out = F.bf16_rne(acc_out)
+    out, acc_out = finalize(w, y2, slot_row)
     return dict(ids=ids, weights=w, token_codes=q, token_scales=s_tok,
                 token_block_scales=sx_tok, offsets=offsets, row_token=row_tok,
                 row_slot=row_slot, slot_row=slot_row, h=h_all, fc2_codes=q2,

@@ -221,4 +221,9 @@ def compare_all(g, r, wl, exact_rows=True):
         assert same > 0.97, same
         assert rel_l2(F.bf16_to_f32(g["fc2_codes"]), F.bf16_to_f32(r["fc2_codes"])) <= 1e-3
     assert rel_l2(g["y2"], r["y2"]) <= 2e-3, rel_l2(g["y2"], r["y2"])
+    # the output is the oracle's finalize of the GPU's own weights and y2
+    # rows, bit for bit (float32 products and slot-order sum, one bf16
+    # rounding); against the oracle's own output it is within the contract
+    fo = O.finalize(g["weights"], g["y2"], g["slot_row"])[0]
+    assert np.array_equal(g["out"], fo), np.count_nonzero(g["out"] != fo)
     return check_output(g["out"], r["out"])

@@ -7,9 +7,10 @@ chosen rows (every row of the last, partial M-tile and of the second 16-row
 group of the first tile, for the hottest, the coldest and random experts:
 the tile tails and the second wave row), against the oracle's pass of that
 one expert; the whole h and y2 rows of the last row of every active expert
-(every expert's last M-tile, every N-tile of both GEMMs); and the bf16 layer output for random tokens, computed token by
-token by the oracle (the layer is independent per token), within the output
-contract.
+(every expert's last M-tile, every N-tile of both GEMMs); the finalize of
+every token from the GPU's own weights and y2 (bit-exact); and the bf16
+layer output for random tokens, computed token by token by the oracle (the
+layer is independent per token), within the output contract.
 
 Only experts that receive tokens are prepared (the others are never read)."""
 import numpy as np
@@ -88,6 +89,9 @@ def test_fullsize_sampled(name):
     assert np.array_equal(g["slot_row"], slot_row.astype(np.int32))
     # GEMM work map (main and tail tiles) from the expert row ranges
     assert np.array_equal(g["tiles"], expected_work_map(off, g["tile_m"]))
+    # the finalize of every token: the oracle's finalize applied to the GPU's
+    # own weights and y2 rows, bit for bit
+    assert np.array_equal(g["out"], O.finalize(g["weights"], g["y2"], g["slot_row"])[0])
     # E4M3 token codes and their scales (per token, or E8M0 per 32) for every token
     if wl.afmt == "fp8":
         q, s = O.quant.e4m3_rows(F.bf16_to_f32(p.hidden))
