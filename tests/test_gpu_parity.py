@@ -43,6 +43,12 @@ SMALL = [
     (1500, 3, 2, 2048, 1536, "mxfp4", "fp8", 39, 0.0),
     (700, 5, 2, 1280, 1024, "mxfp4", "mxfp8", 40, 0.0),
     (600, 8, 2, 1536, 512, "int4", "fp8", 41, 0.0),
+    # 2048+ tokens: the finalize's one-block-per-token form (top-2, top-6 and
+    # the generic top-3 kernel) and a routing index over several 16-chunk
+    # groups, the last one partial
+    (2100, 8, 2, 256, 128, "mxfp4", "fp8", 42, 0.0),
+    (2500, 16, 6, 128, 128, "mxfp4", "bf16", 43, 1.0),
+    (2200, 12, 3, 128, 256, "int4", "fp8", 44, 0.0),
     # W4A4 (MXFP4 activations): every tile configuration, partial scale groups
     (70, 6, 3, 384, 256, "mxfp4", "mxfp4", 51, 0.0),  # 64-row tiles
     (300, 5, 2, 256, 384, "mxfp4", "mxfp4", 52, 2.0), # 160-row tiles, tails
