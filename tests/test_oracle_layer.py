@@ -412,3 +412,28 @@ def test_finalize_pairs_each_slot_weight_with_its_own_expert_row():
     for perm in itertools.permutations(range(k)):
         if list(perm) != list(range(k)):
             assert not close(r["out"], combine(list(perm))), perm
+
+
+def test_finalize_rounds_each_product_to_float32_before_adding():
+    """The finalize keeps the sum in float32 and rounds each weighted term
+    to float32 before the add (no fused multiply-add, no wider sum).  Here
+    w0 * y0 = (1 + 2^-12)^2 = 1 + 2^-11 + 2^-24 is a float32 tie that rounds
+    to 1 + 2^-11 (even mantissa), which the second slot cancels exactly: the
+    float32 sum is 0, while a fused multiply-add or a float64 sum leaves
+    2^-24 (bf16 0x3380)."""
+    a = np.float32(1 + 2.0 ** -12)
+    w = np.array([[a, 1.0]], dtype=np.float32)
+    y2 = np.array([[a], [-(1 + 2.0 ** -11)]], dtype=np.float32)
+    slot_row = np.array([[0, 1]])
+    out, acc = O.finalize(w, y2, slot_row)
+    assert acc.dtype == np.float32 and acc[0, 0] == 0.0
+    assert out[0, 0] == 0
+    assert F.bf16_rne(np.array([2.0 ** -24], dtype=np.float32))[0] == 0x3380
+    # slot order: the same terms in the other order give the same sum here,
+    # and a three-term case where order matters follows the slots
+    w3 = np.array([[1.0, 1.0, 1.0]], dtype=np.float32)
+    y3 = np.array([[2.0 ** 24], [1.0], [-(2.0 ** 24)]], dtype=np.float32)
+    _, acc3 = O.finalize(w3, y3, np.array([[0, 1, 2]]))
+    assert acc3[0, 0] == 0.0  # (2^24 + 1) rounds to 2^24 in float32, then cancels
+    _, acc3b = O.finalize(w3, y3, np.array([[0, 2, 1]]))
+    assert acc3b[0, 0] == 1.0
