@@ -184,8 +184,8 @@ constexpr int kGroupChunks = kRouteGroupChunks;
 static_assert(kGroupChunks * kWave == 1024 && kMaxExperts <= 1024,
               "one count-kernel thread per expert (its scan for a single group)");
 
-// Single block: per-expert totals, chunk bases, expert offsets, tile list.
-// Thread e (blockDim.x == 1024 >= E) holds `run`, the rows of expert e.
+// One block of 1024 threads: expert offsets and the tile list.  Thread e
+// (blockDim.x == 1024 >= E) holds `run`, the rows of expert e.
 // Block-wide exclusive scans of the rows and of the tiles per expert (wave
 // scans + wave totals) give the expert offsets and the work map; returns the
 // first row of expert e.
