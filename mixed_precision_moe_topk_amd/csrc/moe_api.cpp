@@ -510,6 +510,9 @@ moe_status run_checked(const moe_dims* dims, const void* hidden, int64_t num_tok
   g1.K = H;
   g1.N = 2 * I;
   g1.n_tiles = (int32_t)cdiv(2 * I, cfg.bn());
+  // rows averaging a tile or more per expert: adjacent M-tiles are mostly one
+  // expert's, so the block map pairs them per XCD (work_item)
+  g1.pair_m = rows >= (int64_t)L.tile_m * E ? 1 : 0;
   g1.out = h;
   g1.out_stride = I;
   uint8_t* q2 = ws + L.fc2_codes;
@@ -552,6 +555,7 @@ moe_status run_checked(const moe_dims* dims, const void* hidden, int64_t num_tok
   g2.K = I;
   g2.N = H;
   g2.n_tiles = (int32_t)cdiv(H, cfg.bn());
+  g2.pair_m = g1.pair_m;
   g2.out = y2;
   g2.out_stride = H;
   MOE_TRY(hip_check(moe::launch_gemm(variant, false, L.gemm_cfg, g2, L.max_tiles, stream),

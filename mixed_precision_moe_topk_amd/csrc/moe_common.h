@@ -45,27 +45,42 @@ struct Tile {
 };
 
 // Block -> (tile, N-tile) map shared by the GEMM kernels.  Block b runs on
-// XCD b % 8 (each XCD has its own L2); with q = b / 8 and x = b % 8, block b
-// takes M-tile m = 8 (q / n_tiles) + x and N-tile q % n_tiles, so the N-tiles
-// of one M-tile run back to back on one XCD and share its activation rows in
-// that XCD's L2, while neighbouring M-tiles (often one expert's) run at the
-// same time on the other XCDs.  The grid is rounded up to a multiple of
-// 8 * n_tiles blocks (gemm_blocks) so the map covers every item; blocks past
-// the last M-tile return false.  (4 % faster than the plain order b ->
-// (b / n_tiles, b % n_tiles) on the 4096-token prefill GEMM1, equal on the
-// 16384-token one; an XCD-contiguous remap of whole item ranges was slower.)
+// XCD b % 8 (each XCD has its own L2); q = b / 8, x = b % 8.
+//   pair = 0: M-tile m = 8 (q / n_tiles) + x, N-tile q % n_tiles: one M-tile's
+//     N-tiles run back to back on one XCD and share its activation rows in
+//     that L2, while neighbouring M-tiles run at the same time on the other
+//     XCDs (4 % faster than the plain order b -> (b / n_tiles, b % n_tiles) on
+//     the 4096-token prefill GEMM1; an XCD-contiguous remap of whole item
+//     ranges was slower).
+//   pair = 1: the adjacent M-tiles 16 g + 2 x and 16 g + 2 x + 1 (g = q /
+//     (2 n_tiles)) run N-tile major on XCD x, so the two blocks that read one
+//     weight slice start back to back on one L2.  Chosen by the host when the
+//     rows average at least one tile per expert, so that adjacent M-tiles are
+//     mostly one expert's (16384-token prefill, ~5 M-tiles per active expert,
+//     same-box pairs on three boxes: layer -0.5 to -1.7 %, GEMM2 -2 to -3 %,
+//     GEMM1 -2 to +0.6 %; on the shapes whose experts fill one tile it was
+//     0.2-1.3 % slower).
+// The grid is rounded up to a multiple of 16 * n_tiles blocks (gemm_blocks)
+// so either map covers every item; blocks past the last M-tile return false.
 __device__ __forceinline__ bool work_item(const Tile* tiles, const int32_t* num_tiles,
-                                          int32_t n_tiles, Tile* tile, int* nt) {
+                                          int32_t n_tiles, int32_t pair, Tile* tile, int* nt) {
   const int64_t b = blockIdx.x, q = b >> 3, x = b & 7;
-  const int64_t m = (q / n_tiles) * 8 + x;
+  int64_t m;
+  if (pair) {
+    const int64_t g = q / (2 * n_tiles), r = q % (2 * n_tiles);
+    m = 16 * g + 2 * x + (r & 1);
+    *nt = (int)(r >> 1);
+  } else {
+    m = (q / n_tiles) * 8 + x;
+    *nt = (int)(q % n_tiles);
+  }
   if (m >= *num_tiles) return false;
-  *nt = (int)(q % n_tiles);
   *tile = tiles[m];
   return true;
 }
 // Grid size of a GEMM launch covering max_tiles M-tiles (see work_item).
 inline int64_t gemm_blocks(int64_t max_tiles, int32_t n_tiles) {
-  return ((max_tiles + 7) / 8) * 8 * n_tiles;
+  return ((max_tiles + 15) / 16) * 16 * n_tiles;
 }
 
 // ---------------------------------------------------------------- vectors
@@ -194,6 +209,7 @@ struct GemmParams {
   const Tile* tiles;
   const int32_t* num_tiles;
   int32_t n_tiles;             // N / BN
+  int32_t pair_m;              // block map: 1 pairs adjacent M-tiles per XCD (see work_item)
   int32_t K;
   int32_t N;                   // device columns (FC1: 2I interleaved gate/up; FC2: H)
   float* out;                  // FC1: h [rows, N/2]; FC2: y2 [rows, N]

@@ -19,7 +19,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   static_assert(!FC1 || WN % 2 == 0, "FC1 pairs gate/up tiles");
   Tile tile;
   int nt;
-  if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
+  if (!work_item(p.tiles, p.num_tiles, p.n_tiles, p.pair_m, &tile, &nt)) return;
   // wave-uniform values are made scalar: a branch on a per-lane value is an
   // exec-masked branch, after which the compiler waits for every outstanding
   // load (that drained the one-step prefetch before each step's MFMAs)

@@ -296,7 +296,7 @@ __global__ __launch_bounds__(kWave * NW, MINB) void k_gemm_lds(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BM * kKStep];
   Tile tile;
   int nt;
-  if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
+  if (!work_item(p.tiles, p.num_tiles, p.n_tiles, p.pair_m, &tile, &nt)) return;
   const bool full = tile.nrows == BM && (int64_t)(nt + 1) * BN <= p.N;
   if (full) gemm_lds_body<V, FC1, NW, WAVES_M, WM, WN, PB, AD, true>(p, lds, tile, nt);
   else gemm_lds_body<V, FC1, NW, WAVES_M, WM, WN, PB, AD, false>(p, lds, tile, nt);
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(kWave * NW, MINB) void k_gemm_ab(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (BM * kKStep + BN * 64)];
   Tile tile;
   int nt;
-  if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
+  if (!work_item(p.tiles, p.num_tiles, p.n_tiles, p.pair_m, &tile, &nt)) return;
   const bool full = tile.nrows == BM && (int64_t)(nt + 1) * BN <= p.N;
   if (full) gemm_ab_body<V, FC1, NW, WAVES_M, WM, WN, true>(p, lds, tile, nt);
   else gemm_ab_body<V, FC1, NW, WAVES_M, WM, WN, false>(p, lds, tile, nt);
@@ -937,7 +937,7 @@ __global__ __launch_bounds__(dma::kNW * kWave, 1) void k_gemm_dma(GemmParams p) 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[dma::Map<WM, a_blockscaled(V), a_fp4(V)>::kBytes];
   Tile tile;
   int nt;
-  if (!work_item(p.tiles, p.num_tiles, p.n_tiles, &tile, &nt)) return;
+  if (!work_item(p.tiles, p.num_tiles, p.n_tiles, p.pair_m, &tile, &nt)) return;
   gemm_dma_body<V, FC1, WM, PEEL>(p, lds, tile, nt);
 }
 
