@@ -466,9 +466,10 @@ moe_status run_checked(const moe_dims* dims, const void* hidden, int64_t num_tok
   rp.tiles = reinterpret_cast<moe::Tile*>(ws + L.tiles);
   rp.num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
   rp.tile_m = L.tile_m;
-  MOE_TRY(hip_check(moe::launch_route(rp, stream), "route", stream));
-  trace_mark(tc, 1, stream);
 
+  // Routing and the token quantisation: for E4M3 / MX activations the router
+  // and the quantiser share one launch (independent inputs), so the "route"
+  // stage of a trace holds both and the "quant" stage is empty.
   const float* tok_scales = nullptr;
   const uint8_t* tok_bscales = nullptr;
   const uint8_t* a1 = static_cast<const uint8_t*>(hidden);
@@ -477,15 +478,18 @@ moe_status run_checked(const moe_dims* dims, const void* hidden, int64_t num_tok
     uint8_t* codes = ws + L.tok_codes;
     float* sc = reinterpret_cast<float*>(ws + L.tok_scales);
     uint8_t* bsc = mx ? ws + L.tok_bscales : nullptr;
-    MOE_TRY(hip_check(moe::launch_quant_tokens(static_cast<const uint16_t*>(hidden), T, H,
-                                               mx ? mx_mode : moe::kQuantFp8Row,
-                                               codes, sc, bsc, stream),
-                      "quantize tokens", stream));
+    MOE_TRY(hip_check(moe::launch_router_quant(rp, static_cast<const uint16_t*>(hidden), H,
+                                               mx ? mx_mode : moe::kQuantFp8Row, codes, sc,
+                                               bsc, stream),
+                      "route + quantize tokens", stream));
     if (fp8) tok_scales = sc;
     tok_bscales = bsc;
     a1 = codes;
     a1_stride = e2m1 ? H / 2 : H;
+  } else {
+    MOE_TRY(hip_check(moe::launch_route(rp, stream), "route", stream));
   }
+  trace_mark(tc, 1, stream);
   trace_mark(tc, 2, stream);
 
   const int variant = variant_of(dims);

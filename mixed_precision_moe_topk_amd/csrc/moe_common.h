@@ -238,12 +238,20 @@ __host__ __device__ constexpr int64_t mx_scale_offset(int64_t kb) {  // kb = col
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_route(const RouteParams& p, hipStream_t st);
+// The routing index alone (the kernels after the router): count / scan /
+// scatter, or the single-block kernel for at most 64 tokens.
+hipError_t launch_route_index(const RouteParams& p, hipStream_t st);
 // Activation quantisation modes of the token and FC2-input quantisers.
 enum QuantMode : int { kQuantFp8Row = 0, kQuantBf16 = 1, kQuantMxfp8 = 2, kQuantMxfp4 = 3 };
 // FP8 rows: codes + one float scale per row; MXFP8 / MXFP4: E4M3 codes [C] /
 // packed E2M1 codes [C/2] + E8M0 per 32 (bscales [rows][mx_scale_row_bytes(C)]
 // in MFMA scale order, row scales written as 1.0); BF16: bits, scale 1.
 hipError_t launch_quant_tokens(const uint16_t* x, int64_t T, int32_t H, int mode,
+                               uint8_t* codes, float* scales, uint8_t* bscales, hipStream_t st);
+// The router and the token quantiser (mode kQuantFp8Row / kQuantMxfp8 /
+// kQuantMxfp4) in one launch, then the routing index: the same outputs as
+// launch_route followed by launch_quant_tokens.
+hipError_t launch_router_quant(const RouteParams& p, const uint16_t* x, int32_t H, int mode,
                                uint8_t* codes, float* scales, uint8_t* bscales, hipStream_t st);
 hipError_t launch_requant(const float* h, int64_t rows, int32_t I, int mode, uint8_t* codes,
                           float* scales, uint8_t* bscales, hipStream_t st);

@@ -10,7 +10,7 @@
 // SwiGLU output is requantised the same way per expanded row before FC2.
 // PR #4793 ("Unify MoE CuTe DSL dispatch to be dtype agnostic") fuses the
 // router-weighted sum of the k expert outputs into a finalize step.
-#include "moe_common.h"
+#include "moe_router.h"
 
 namespace moe {
 
@@ -52,12 +52,11 @@ __device__ __forceinline__ uint2 bf16x8_to_e4m3(const uint4& u, float s, float i
 // One block per token row: x bf16 [T, H] -> codes E4M3 [T, H], scales [T].
 // H % 8 == 0.  Rows of up to 8192 elements are read once and kept in
 // registers between the amax and the quantisation; longer rows are read twice.
-__global__ __launch_bounds__(256) void k_quant_tokens(const uint16_t* __restrict__ x, int32_t H,
-                                                      uint8_t* __restrict__ codes,
-                                                      float* __restrict__ scales) {
-  __shared__ float red[4];
+__device__ __forceinline__ void quant_token_row(const uint16_t* __restrict__ x, int32_t H,
+                                                uint8_t* __restrict__ codes,
+                                                float* __restrict__ scales, const int64_t t,
+                                                float* red) {
   constexpr int kR = 4;  // uint4 (8 bf16) per thread kept in registers
-  const int64_t t = blockIdx.x;
   const uint4* row = reinterpret_cast<const uint4*>(x + t * H);
   uint2* out = reinterpret_cast<uint2*>(codes + t * H);
   const int nv = H / 8;
@@ -88,6 +87,13 @@ __global__ __launch_bounds__(256) void k_quant_tokens(const uint16_t* __restrict
   const float inv = __fdiv_rn(1.0f, s);
   for (int i = threadIdx.x; i < nv; i += blockDim.x) out[i] = bf16x8_to_e4m3(row[i], s, inv);
   if (threadIdx.x == 0) scales[t] = s;
+}
+
+__global__ __launch_bounds__(256) void k_quant_tokens(const uint16_t* __restrict__ x, int32_t H,
+                                                      uint8_t* __restrict__ codes,
+                                                      float* __restrict__ scales) {
+  __shared__ float red[4];
+  quant_token_row(x, H, codes, scales, blockIdx.x, red);
 }
 
 // One block per expanded row: h f32 [rows, I] -> FC2 input.
@@ -196,11 +202,10 @@ __device__ __forceinline__ uint2 mx_quant8(const float (&v)[8], bool valid, uint
 // codes [C/2]) + E8M0 codes in the block-scaled MFMA's scale order
 // (mx_scale_offset); the row's float scale is written as 1.0.
 template <bool SRC_BF16, bool E2M1>
-__global__ __launch_bounds__(256) void k_quant_mx(const void* __restrict__ src, int32_t C,
-                                                  uint8_t* __restrict__ codes,
-                                                  uint8_t* __restrict__ bscales,
-                                                  float* __restrict__ scales) {
-  const int64_t r = blockIdx.x;
+__device__ __forceinline__ void quant_mx_row(const void* __restrict__ src, int32_t C,
+                                             uint8_t* __restrict__ codes,
+                                             uint8_t* __restrict__ bscales,
+                                             float* __restrict__ scales, const int64_t r) {
   for (int i = threadIdx.x; 8 * (i - (int)(threadIdx.x & 3)) < C; i += 256) {
     const bool valid = 8 * i < C;
     float v[8];
@@ -229,6 +234,65 @@ __global__ __launch_bounds__(256) void k_quant_mx(const void* __restrict__ src, 
     }
   }
   if (threadIdx.x == 0) scales[r] = 1.0f;
+}
+
+template <bool SRC_BF16, bool E2M1>
+__global__ __launch_bounds__(256) void k_quant_mx(const void* __restrict__ src, int32_t C,
+                                                  uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ bscales,
+                                                  float* __restrict__ scales) {
+  quant_mx_row<SRC_BF16, E2M1>(src, C, codes, bscales, scales, blockIdx.x);
+}
+
+// The router and the token quantiser in one launch: they read different
+// inputs (logits, hidden states) and the routing index waits only for the
+// router, so the first ceil(T / 4) blocks route four tokens each and the
+// next T blocks quantise one token each (QM 0: per-token E4M3, 1: MXFP8, 2:
+// MXFP4).  The two kernels back to back cost the router's time on top of the
+// quantiser's.
+template <int PER, int QM>
+__global__ __launch_bounds__(256) void k_router_quant(RouteParams p, const uint16_t* __restrict__ x,
+                                                      int32_t H, uint8_t* __restrict__ codes,
+                                                      float* __restrict__ scales,
+                                                      uint8_t* __restrict__ bscales,
+                                                      int64_t router_blocks) {
+  __shared__ float red[4];
+  if ((int64_t)blockIdx.x < router_blocks) {
+    const int64_t t = (int64_t)blockIdx.x * kRouterWaves + threadIdx.x / kWave;
+    if (t < p.tokens) route_token<PER>(p, t);
+    return;
+  }
+  const int64_t t = (int64_t)blockIdx.x - router_blocks;
+  if constexpr (QM == 0) quant_token_row(x, H, codes, scales, t, red);
+  else quant_mx_row<true, QM == 2>(x, H, codes, bscales, scales, t);
+}
+
+template <int QM>
+static void launch_rq(const RouteParams& p, const uint16_t* x, int32_t H, uint8_t* codes,
+                      float* scales, uint8_t* bscales, hipStream_t st) {
+  const int64_t rb = (p.tokens + kRouterWaves - 1) / kRouterWaves;
+  const unsigned grid = (unsigned)(rb + p.tokens);
+  switch (router_per(p.experts)) {
+    case 1: k_router_quant<1, QM><<<grid, 256, 0, st>>>(p, x, H, codes, scales, bscales, rb); break;
+    case 2: k_router_quant<2, QM><<<grid, 256, 0, st>>>(p, x, H, codes, scales, bscales, rb); break;
+    case 3: k_router_quant<3, QM><<<grid, 256, 0, st>>>(p, x, H, codes, scales, bscales, rb); break;
+    case 4: k_router_quant<4, QM><<<grid, 256, 0, st>>>(p, x, H, codes, scales, bscales, rb); break;
+    case 6: k_router_quant<6, QM><<<grid, 256, 0, st>>>(p, x, H, codes, scales, bscales, rb); break;
+    case 8: k_router_quant<8, QM><<<grid, 256, 0, st>>>(p, x, H, codes, scales, bscales, rb); break;
+    case 12: k_router_quant<12, QM><<<grid, 256, 0, st>>>(p, x, H, codes, scales, bscales, rb); break;
+    default: k_router_quant<16, QM><<<grid, 256, 0, st>>>(p, x, H, codes, scales, bscales, rb); break;
+  }
+}
+
+hipError_t launch_router_quant(const RouteParams& p, const uint16_t* x, int32_t H, int mode,
+                               uint8_t* codes, float* scales, uint8_t* bscales, hipStream_t st) {
+  if (p.tokens == 0) return hipSuccess;
+  static_assert(kRouterWaves * kWave == 256, "router blocks are quantiser-sized");
+  if (mode == kQuantMxfp8) launch_rq<1>(p, x, H, codes, scales, bscales, st);
+  else if (mode == kQuantMxfp4) launch_rq<2>(p, x, H, codes, scales, bscales, st);
+  else launch_rq<0>(p, x, H, codes, scales, bscales, st);
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : launch_route_index(p, st);
 }
 
 // Blocks (t, y): out[t] = bf16(sum_j fl32(w[t,j] * y2[row(t,j)])), the float32
