@@ -367,8 +367,11 @@ moe_status moe_autotune(const moe_dims* dims, const void* hidden, int64_t num_to
  * At most 4096 calls are kept; later calls are not recorded.  An unknown
  * mode returns MOE_ERR_INVALID_ARG.  Not for use under HIP graph capture. */
 typedef enum {
-  MOE_STAGE_ROUTE = 0,    /* router, routing index, work map */
-  MOE_STAGE_QUANT = 1,    /* per-token E4M3 quantisation (FP8 activations) */
+  MOE_STAGE_ROUTE = 0,    /* router, routing index, work map; for E4M3 and MX
+                             activations also the token quantisation, which
+                             shares the router's launch */
+  MOE_STAGE_QUANT = 1,    /* nothing (the token quantisation runs in the
+                             route stage; kept so stage indices stay fixed) */
   MOE_STAGE_GEMM1 = 2,    /* grouped GEMM1 + SwiGLU */
   MOE_STAGE_REQUANT = 3,  /* FC2 input (nothing when GEMM1 writes it, fc2_fused) */
   MOE_STAGE_GEMM2 = 4,    /* grouped GEMM2 */
